@@ -1,0 +1,352 @@
+"""Pins that hold the CPU oracle to the GRINQH note and to mathematics.
+
+No pin retypes the oracle's own formulas: each compares it with something
+else - values derived by hand from the page (tests/golden), a library
+routine the special case reduces to, a closed form, an invariant, or a brute
+force that reaches the same number by a different mechanism (bit strings,
+enumeration of truncation intervals).
+
+"KD1/KD2/KD3" are items 1-3 of the key-design section (方法详解 / 关键设计) of
+"GRINQH: Graded Input-Based Quantization Hierarchy for Efficient LLM
+Generation" (papernotes.org note).
+"""
+
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import grinqh_oracle as O
+from oracle import c_oracle as C
+import synthetic as S
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- KD1 -------
+
+def test_assign_bits_golden_ties(golden_dir):
+    g = _load(golden_dir, "assign_bits_ties.json")
+    x = np.array([float(v) for v in g["x"]], dtype=np.float32)
+    bits = O.assign_bits(x, np.array(g["theta"], np.float32), g["b_max"])
+    assert bits.tolist() == g["bits"]
+    assert C.assign_bits(x, np.array(g["theta"], np.float32), g["b_max"]).tolist() == g["bits"]
+
+
+@pytest.mark.parametrize("b_max", [2, 4, 6, 8])
+def test_assign_bits_is_searchsorted(b_max):
+    """For finite x and ascending thresholds, the level is numpy's right-side
+    insertion index of |x| into the thresholds (interval [theta_k, theta_k+1))."""
+    rng = np.random.default_rng(7 + b_max)
+    P = b_max // 2
+    theta = np.sort(rng.uniform(0.0, 3.0, P)).astype(np.float32)
+    x = rng.standard_normal(20000).astype(np.float32) * 2
+    # exact ties, one ulp either side, signed zeros
+    ties = np.concatenate([theta, -theta, np.nextafter(theta, np.float32(0)),
+                           np.nextafter(theta, np.float32(np.inf)), [0.0, -0.0]]).astype(np.float32)
+    x = np.concatenate([x, ties])
+    expect = 2 * np.searchsorted(theta.astype(np.float64), np.abs(x.astype(np.float64)), side="right")
+    assert np.array_equal(O.assign_bits(x, theta, b_max), expect.astype(np.uint8))
+    assert np.array_equal(C.assign_bits(x, theta, b_max), expect.astype(np.uint8))
+
+
+def test_assign_bits_special_values():
+    theta = np.array([0.0, 0.0, 1.0, 1.0], np.float32)   # equal thresholds: empty levels
+    x = np.array([0.0, -0.0, 0.5, 1.0, np.nan, np.inf], np.float32)
+    # |x| >= 0 always (level 2 at least), NaN compares false everywhere
+    assert O.assign_bits(x, theta, 8).tolist() == [4, 4, 4, 8, 0, 8]
+    assert O.active_channels(O.assign_bits(x, theta, 8)).tolist() == [0, 1, 2, 3, 5]
+
+
+# ---------------------------------------------------------------- KD2 -------
+
+def test_pack_golden_hand_examples(golden_dir):
+    g = _load(golden_dir, "pack_hand_example.json")
+    for case in g["cases"]:
+        q = np.array(case["q_out_by_in"], dtype=np.uint8)
+        expect = np.array(case["planes"], dtype=np.uint32)
+        assert np.array_equal(O.pack_planes(q, case["b_max"]), expect)
+        assert np.array_equal(C.pack_planes(q, case["b_max"]), expect)
+
+
+@pytest.mark.parametrize("b_max,d_in,d_out", [(8, 5, 1), (8, 3, 130), (4, 7, 64), (6, 2, 65), (2, 9, 200)])
+def test_pack_round_trip(b_max, d_in, d_out):
+    rng = np.random.default_rng(b_max * 1000 + d_out)
+    q = rng.integers(0, 1 << b_max, size=(d_out, d_in), dtype=np.uint8)
+    q[0, 0] = 0
+    q[-1, -1] = (1 << b_max) - 1
+    planes = O.pack_planes(q, b_max)
+    assert planes.shape == (d_in, b_max // 2, O.row_words(d_out))
+    frag = O.unpack_fragments(planes, d_out).astype(np.int64)
+    P = b_max // 2
+    rebuilt = sum(frag[:, p, :] << (b_max - 2 * p - 2) for p in range(P))
+    assert np.array_equal(rebuilt, q.T.astype(np.int64))
+    # padding fragments are zero
+    full = ((planes[:, :, :, None] >> (2 * np.arange(16, dtype=np.uint32))) & 3).reshape(d_in, P, -1)
+    assert not full[:, :, d_out:].any()
+    assert np.array_equal(C.pack_planes(q, b_max), planes)
+
+
+# ---------------------------------------------------------------- KD3 -------
+
+def _string_truncate(q, b, b_max):
+    """Top b bits of q by string slicing, then zero-filled: a different mechanism."""
+    s = format(int(q), f"0{b_max}b")
+    return int(s[:b] + "0" * (b_max - b), 2) if b else 0
+
+
+@pytest.mark.parametrize("b_max", [2, 4, 6, 8])
+def test_codes_exhaustive(b_max):
+    """Every code q and every width b: the sum of the taken planes equals the
+    zero-filled top-b-bit string of q (KD3's spliced truncated integer)."""
+    q = np.arange(1 << b_max, dtype=np.uint8)[:, None]          # d_out = 2^b_max, d_in = 1
+    planes = O.pack_planes(q, b_max)
+    for b in range(2, b_max + 1, 2):
+        bits = np.array([b])
+        from_planes = O.codes_from_planes(planes, bits, b_max, q.shape[0])[0]
+        direct = O.truncated_codes(q, bits, b_max)[0]
+        expect = [_string_truncate(v, b, b_max) for v in range(1 << b_max)]
+        assert from_planes.tolist() == expect
+        assert direct.tolist() == expect
+
+
+@pytest.mark.parametrize("b_max", [2, 4, 6, 8])
+def test_midpoint_is_interval_centroid(b_max):
+    """w_hat_b(q) equals the mean of the full-width reconstructions s*(r + 1/2) + z
+    over every code r that shares q's top b bits (brute-force enumeration), i.e.
+    phi puts the point in the middle of the truncation interval (KD3)."""
+    s, z = 0.0068359375, -0.0031280517578125      # fp16-exact values
+    for b in range(2, b_max + 1, 2):
+        k = b_max - b
+        bits = np.array([b])
+        for qv in range(1 << b_max):
+            code = O.truncated_codes(np.array([[qv]], np.uint8), bits, b_max)[0, 0]
+            w = O.dequant(np.array([[code]]), bits, [s], [z], b_max)[0, 0]
+            top = qv >> k
+            members = [r for r in range(1 << b_max) if (r >> k) == top]
+            assert len(members) == 1 << k
+            centroid = np.mean([s * (r + 0.5) + z for r in members])
+            assert w == pytest.approx(centroid, rel=0, abs=1e-15)
+
+
+def test_bias_table_closed_forms(golden_dir):
+    g = _load(golden_dir, "bias_closed_forms.json")
+    for b_max_s, table in g["tables"].items():
+        got = O.bias_table(int(b_max_s))
+        for b_s, row in table.items():
+            for key, val in row.items():
+                assert got[int(b_s)][key] == pytest.approx(val, abs=1e-12), (b_max_s, b_s, key)
+
+
+# ------------------------------------------------------------- GEMV ---------
+
+def test_tiny_gemv_golden(golden_dir):
+    g = _load(golden_dir, "tiny_gemv_b4.json")
+    q = np.array(g["q_out_by_in"], np.uint8)
+    x = np.array(g["x"], np.float32)
+    th = np.array(g["theta"], np.float32)
+    bits = O.assign_bits(x, th, g["b_max"])
+    assert bits.tolist() == g["bits"]
+    codes = O.truncated_codes(q, bits, g["b_max"])
+    assert codes.tolist() == g["codes_in_by_out"]
+    w = O.dequant(codes, bits, g["s"], g["z"], g["b_max"])
+    assert np.allclose(w, g["w_hat_in_by_out"], rtol=0, atol=1e-15)
+    for y in (O.gemv(x, th, q, g["s"], g["z"], g["b_max"]),
+              O.gemv(x, th, q, g["s"], g["z"], g["b_max"], exact=True),
+              O.gemv_from_planes(x, th, O.pack_planes(q, g["b_max"]), g["s"], g["z"], g["b_max"], 2),
+              C.gemv(x, th, q, g["s"], g["z"], g["b_max"])):
+        assert np.allclose(y, g["y"], rtol=0, atol=1e-15)
+    assert O.eff_bits(bits) == g["eff_bits"]
+
+
+def _rand_problem(d_in, d_out, b_max, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 1 << b_max, size=(d_out, d_in), dtype=np.uint8)
+    s = rng.uniform(0.001, 0.01, d_out).astype(np.float16)
+    z = rng.normal(0, 0.01, d_out).astype(np.float16)
+    x = (rng.standard_t(3, d_in)).astype(np.float32)
+    theta = np.sort(np.quantile(np.abs(x), np.linspace(0.2, 0.9, b_max // 2))).astype(np.float32)
+    return q, s, z, x, theta
+
+
+@pytest.mark.parametrize("b_max", [2, 4, 6, 8])
+def test_dense_mode_is_plain_dot(b_max):
+    """All thresholds 0 -> every channel gets b_max bits; the product is numpy's
+    dot of x with s_j*(q_ji + 1/2) + z_j built from q directly, never packed."""
+    q, s, z, x, _ = _rand_problem(300, 70, b_max, 11)
+    theta = np.zeros(b_max // 2, np.float32)
+    W = s.astype(np.float64)[None, :] * (q.T.astype(np.float64) + 0.5) + z.astype(np.float64)[None, :]
+    ref = np.dot(x.astype(np.float64), W)
+    y = O.gemv(x, theta, q, s, z, b_max)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+    yc = C.gemv(x, theta, q, s, z, b_max)
+    assert np.max(np.abs(yc - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_all_skipped_gives_exact_zero():
+    q, s, z, x, _ = _rand_problem(200, 64, 8, 12)
+    for theta in (np.full(4, np.inf, np.float32), np.full(4, 1e30, np.float32)):
+        bits = O.assign_bits(x, theta, 8)
+        assert O.active_channels(bits).size == 0
+        assert np.all(O.gemv(x, theta, q, s, z, 8) == 0.0)
+        assert np.all(C.gemv(x, theta, q, s, z, 8) == 0.0)
+        assert O.required_bytes(bits, 64)["planes"] == 0.0
+
+
+def test_single_active_channel():
+    q, s, z, x, _ = _rand_problem(50, 64, 8, 13)
+    x[:] = 0.01
+    x[17] = -3.0
+    theta = np.array([1.0, 2.0, 2.5, 9.0], np.float32)    # only |x_17| = 3 passes, 6 bits
+    y = O.gemv(x, theta, q, s, z, 8)
+    # 6 bits: k = 2, code = top six bits, midpoint offset = 2
+    row = [float(s[j]) * (((int(q[j, 17]) >> 2) << 2) + 2.0) + float(z[j]) for j in range(64)]
+    assert np.allclose(y, -3.0 * np.array(row, np.float64), rtol=1e-15, atol=0)
+
+
+def test_bruteforce_8x8_all_level_patterns():
+    """All 5^8 assignments of the 8 channels to the 5 levels of b_max = 8.
+    Reference: per channel and level, the reconstructed row is the centroid of
+    the full-width reconstructions over the truncation interval (enumerated),
+    and y sums x_i times that row over channels with a non-zero level."""
+    b_max, d = 8, 8
+    rng = np.random.default_rng(88)
+    q = rng.integers(0, 256, size=(d, d), dtype=np.uint8)
+    s = rng.uniform(0.001, 0.01, d).astype(np.float16).astype(np.float64)
+    z = rng.normal(0, 0.01, d).astype(np.float16).astype(np.float64)
+    theta = np.array([0.5, 1.0, 2.0, 4.0], np.float32)
+    mid = np.array([0.25, 0.75, 1.5, 3.0, 6.0])               # one magnitude inside each level
+    # R[i, L, j]: reconstructed weight of channel i at level L (0 -> none)
+    R = np.zeros((d, 5, d))
+    for i in range(d):
+        for L in range(1, 5):
+            k = b_max - 2 * L
+            for j in range(d):
+                top = int(q[j, i]) >> k
+                members = [r for r in range(256) if (r >> k) == top]
+                R[i, L, j] = np.mean([s[j] * (r + 0.5) + z[j] for r in members])
+    levels = np.array(list(itertools.product(range(5), repeat=d)), dtype=np.int64)   # [5^8][8]
+    signs = np.where(rng.random(levels.shape) < 0.5, -1.0, 1.0)
+    X = (signs * mid[levels]).astype(np.float32)
+    ref = np.einsum("ni,nij->nj", X.astype(np.float64), R[np.arange(d)[None, :], levels, :])
+    for lo in range(0, levels.shape[0], 65536):
+        sl = slice(lo, lo + 65536)
+        bits = O.assign_bits(X[sl], theta, b_max)
+        assert np.array_equal(bits.astype(np.int64), 2 * levels[sl])
+        y = O.gemv(X[sl], theta, q, s, z, b_max)
+        assert np.max(np.abs(y - ref[sl])) <= 1e-12
+    # the plane path and the C oracle on a sample of the patterns
+    planes = O.pack_planes(q, b_max)
+    for n in rng.choice(levels.shape[0], 300, replace=False):
+        yp = O.gemv_from_planes(X[n], theta, planes, s, z, b_max, d)
+        yc = C.gemv(X[n], theta, q, s, z, b_max)
+        assert np.max(np.abs(yp - ref[n])) <= 1e-12
+        assert np.max(np.abs(yc - ref[n])) <= 1e-12
+
+
+def test_power_of_two_scale_invariance_and_permutation():
+    q, s, z, x, theta = _rand_problem(513, 130, 8, 14)
+    y = O.gemv(x, theta, q, s, z, 8)
+    for m in (-3, 5):
+        xs = np.ldexp(x, m).astype(np.float32)
+        ts = np.ldexp(theta, m).astype(np.float32)
+        assert np.array_equal(O.assign_bits(xs, ts, 8), O.assign_bits(x, theta, 8))
+        assert np.array_equal(O.gemv(xs, ts, q, s, z, 8), np.ldexp(y, m))
+    perm = np.random.default_rng(3).permutation(513)
+    yp = O.gemv(x[perm], theta, q[:, perm], s, z, 8)
+    assert np.max(np.abs(yp - y)) <= 1e-12 * np.max(np.abs(y))
+
+
+@pytest.mark.parametrize("b_max", [4, 8])
+def test_factorised_form(b_max):
+    """y_j = s_j*(A_j + C) + z_j*S with A from the raw plane fragments weighted by
+    x_i*4^(P-1-p), C = sum x_i*phi_i and S = sum x_i over loaded channels: the
+    algebra a kernel can use, equal to the oracle's plain sum to 1e-12."""
+    q, s, z, x, theta = _rand_problem(700, 200, b_max, 15)
+    P = b_max // 2
+    bits = O.assign_bits(x, theta, b_max)
+    frag = O.unpack_fragments(O.pack_planes(q, b_max), 200).astype(np.float64)
+    xd = x.astype(np.float64)
+    A = np.zeros(200)
+    Cs = 0.0
+    Ss = 0.0
+    for i in range(700):
+        Pi = int(bits[i]) // 2
+        if Pi == 0:
+            continue
+        for p in range(Pi):
+            A += xd[i] * 4.0 ** (P - 1 - p) * frag[i, p]
+        Cs += xd[i] * 2.0 ** (b_max - int(bits[i]) - 1)
+        Ss += xd[i]
+    yf = s.astype(np.float64) * (A + Cs) + z.astype(np.float64) * Ss
+    y = O.gemv(x, theta, q, s, z, b_max)
+    assert np.max(np.abs(yf - y)) <= 1e-12 * np.max(np.abs(y))
+
+
+def test_required_bytes_counts_taken_plane_rows():
+    q, s, z, x, theta = _rand_problem(999, 192, 8, 16)
+    bits = O.assign_bits(x, theta, 8)
+    rows = int(np.sum(bits // 2))
+    rb = O.required_bytes(bits, 192)
+    assert rb["planes"] == rows * O.row_words(192) * 4
+    assert rb["total"] == rb["planes"] + 4 * 192
+
+
+def test_nan_is_skipped_and_inf_propagates():
+    q, s, z, x, theta = _rand_problem(64, 64, 8, 17)
+    assert theta[0] > 0
+    x_nan = x.copy()
+    x_nan[5] = np.nan
+    x_off = x.copy()
+    x_off[5] = 0.0                       # below theta_1: not loaded
+    assert O.assign_bits(x_nan, theta, 8)[5] == 0
+    y_nan = O.gemv(x_nan, theta, q, s, z, 8)
+    assert np.all(np.isfinite(y_nan))
+    assert np.array_equal(y_nan, O.gemv(x_off, theta, q, s, z, 8))
+    x_inf = x.copy()
+    x_inf[3] = np.inf
+    assert O.assign_bits(x_inf, theta, 8)[3] == 8
+    assert not np.all(np.isfinite(O.gemv(x_inf, theta, q, s, z, 8)))
+
+
+def test_c_oracle_matches_numpy_on_small_workload():
+    L = S.make_linear(S.small_case())
+    y = O.gemv(L.x, L.theta, L.q, L.s, L.z, 8)
+    yc = C.gemv(L.x, L.theta, L.q, L.s, L.z, 8)
+    assert np.max(np.abs(y - yc)) <= 1e-12 * np.max(np.abs(y))
+    assert np.array_equal(O.pack_planes(L.q, 8), C.pack_planes(L.q, 8))
+
+
+def test_synthetic_thresholds_hit_target_bits():
+    L = S.make_linear(S.small_case())
+    assert abs(O.eff_bits(O.assign_bits(L.x, L.theta, 8)) - 3.1) < 0.25
+    for eff in (2, 3, 4):
+        spec = S.llama8b_linears(eff)[0]
+        Lx = S.make_linear(spec, with_codes=False)
+        assert abs(O.eff_bits(O.assign_bits(Lx.x, Lx.theta, 8)) - eff) < 0.2
+    Ld = S.make_linear(S.llama8b_linears(8)[0], with_codes=False)
+    assert O.eff_bits(O.assign_bits(Ld.x, Ld.theta, 8)) == 8.0
+
+
+def test_max_rel_error_metric():
+    ref = np.array([1.0, -2.0, 0.0, 1e-9])
+    assert O.max_rel_error(ref, ref) == 0.0
+    rms = np.sqrt(np.mean(ref ** 2))
+    y = ref + np.array([0, 0, 1e-3 * rms, 0])
+    assert O.max_rel_error(y, ref) == pytest.approx(0.1, rel=1e-9)
+
+
+def test_round_to_bf16_against_bit_arithmetic():
+    """RNE to bf16 checked on hand-picked halfway cases and against numpy's own
+    fp32 -> fp16-free route: exact values with <= 8 significant bits round-trip."""
+    vals = np.array([1.0, 1.00390625, 1.01171875, -3.0, 0.0], np.float32)
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7 -> even (1.0);
+    # 1 + 3*2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6 -> even (1 + 2^-6)
+    got = O.round_to_bf16(vals)
+    back = (got.astype(np.uint32) << 16).view(np.float32)
+    assert back.tolist() == [1.0, 1.0, 1.015625, -3.0, 0.0]
