@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the GRINQH decode GEMV on one MI355X.
+
+One step = the three 8B-shaped decode linears (4096->4096, 4096->14336,
+14336->4096; b_max 8; bf16 x ~ Student-t(3); per-output fp16 s, z; bf16 y)
+at about 3 effective bits, each one grinqh_gemv call (bit assignment,
+prefix-plane streaming, midpoint dequant and the product, all in the HIP
+library).  Inputs are resident in HBM before timing starts.  The steps rotate
+over enough packed weight copies (>= 512 MB) that the 256 MB Infinity Cache
+cannot hold them.  The timed region is one HIP graph holding exactly K steps,
+bracketed by device synchronisation and HIP events on the launch stream.
+
+Reported value: required bytes per second, where required bytes = taken
+2-bit planes (sum_i b_i * d_out / 8) + fp16 s and z (4 * d_out), summed over
+the step's GEMVs.  Also reported: the effective-bits sweep 2/3/4/8 (8 = all
+channels at b_max, the dense dequant GEMV of the same kernel), and the plain
+fp64 C oracle timed on the host cores over a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMV µs and required-bytes HBM GB/s (% of MI355X peak) at 2/3/4/8 eff. bits"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def required_bytes(bits_np: np.ndarray, d_out: int) -> float:
+    return float(bits_np.astype(np.int64).sum()) * d_out / 8.0 + 4.0 * d_out
+
+
+class Shape:
+    def __init__(self, spec, n_copies, dev, effs):
+        import torch
+        import input_adaptive_bit_amd as G
+        import synthetic as S
+        self.spec = spec
+        self.d_in, self.d_out = spec.d_in, spec.d_out
+        lin = S.make_linear(spec)
+        self.q0 = lin.q                                  # host codes of copy 0 (CPU baseline)
+        self.s_np, self.z_np, self.x_f32 = lin.s, lin.z, lin.x
+        self.L = G.grinqh_layout_init(spec.d_in, spec.d_out, spec.b_max)
+        self.planes = []
+        for c in range(n_copies):
+            q = lin.q if c == 0 else S.gen_codes(spec, role=10 + c)
+            qd = torch.from_numpy(q).to(dev)
+            _, pl = G.pack(qd, spec.b_max)
+            self.planes.append(pl)
+            del qd
+        torch.cuda.synchronize()
+        self.s = torch.from_numpy(lin.s).to(dev)
+        self.z = torch.from_numpy(lin.z).to(dev)
+        self.x = torch.from_numpy(lin.x_bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        self.ws = G.new_workspace(self.L, dev)
+        self.y = torch.empty(spec.d_out, dtype=torch.bfloat16, device=dev)
+        # thresholds per effective-bits target (same codes, scales and x for every target)
+        self.theta = {}
+        self.theta_np = {}
+        for eff, sp in effs.items():
+            th = S.make_linear(sp, with_codes=False).theta
+            self.theta_np[eff] = th
+            self.theta[eff] = torch.from_numpy(th).to(dev)
+        self.bits = {}
+        self.req = {}
+        for eff in effs:
+            bits, _, _ = G.assign_bits(self.L, self.x, self.theta[eff])
+            torch.cuda.synchronize()
+            b = bits.cpu().numpy()
+            self.bits[eff] = b
+            self.req[eff] = required_bytes(b, self.d_out)
+
+    def launch(self, copy: int, eff) -> None:
+        import input_adaptive_bit_amd as G
+        G.grinqh_gemv(self.L, self.x, self.theta[eff], self.planes[copy], self.s, self.z, self.y, self.ws)
+
+
+def capture(fn):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def time_graph(g, reps: int = 1) -> float:
+    """Milliseconds for `reps` replays, events on the current stream."""
+    import torch
+    st = torch.cuda.Event(enable_timing=True)
+    en = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    st.record()
+    for _ in range(reps):
+        g.replay()
+    en.record()
+    torch.cuda.synchronize()
+    return st.elapsed_time(en)
+
+
+def cpu_baseline(shapes, eff, seconds: float):
+    from oracle import c_oracle
+    per_step = sum(sh.req[eff] for sh in shapes)
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        for sh in shapes:
+            c_oracle.gemv(sh.x_f32, sh.theta_np[eff], sh.q0, sh.s_np, sh.z_np, sh.spec.b_max)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {
+        "value": round(per_step * passes / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{passes} full passes of the 3 linears at ~{eff} eff. bits "
+                   f"(plain fp64 C oracle, one thread, {el:.1f} s)"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--eff", type=int, default=3, choices=[2, 3, 4, 8])
+    ap.add_argument("--sweep-reps", type=int, default=64, help="launches per (eff, shape) sweep point")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copies", type=int, default=0, help="weight copies (0: enough for 512 MB)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): this decode GEMV is "
+              "built and measured on a single MI355X; see the sharding notes in DESIGN.md.", flush=True)
+        return 2
+
+    import torch
+    import input_adaptive_bit_amd as G
+    import synthetic as S
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    G.load()
+    dev = torch.device("cuda:0")
+    effs = {e: None for e in (2, 3, 4, 8)}
+    per_eff_specs = {e: S.llama8b_linears(e) for e in effs}
+    set_bytes = sum(4096 * 4096 + 4096 * 14336 + 14336 * 4096 for _ in [0])   # b_max 8: 1 byte/weight
+    n_copies = args.copies or max(1, math.ceil(2 * MALL_BYTES / set_bytes))
+    log(f"setup: {n_copies} weight copies of {set_bytes / 1e6:.1f} MB")
+    shapes = []
+    for k in range(3):
+        sp = {e: per_eff_specs[e][k] for e in effs}
+        shapes.append(Shape(sp[args.eff], n_copies, dev, sp))
+    eff = args.eff
+
+    def steps_fn(n):
+        def run():
+            for st in range(n):
+                c = st % n_copies
+                for sh in shapes:
+                    sh.launch(c, eff)
+        return run
+
+    # warmup (eager, fills caches/JIT paths), then the two graphs
+    steps_fn(2)()
+    torch.cuda.synchronize()
+    g_warm = capture(steps_fn(max(1, args.warmup))) if args.warmup > 0 else None
+    g_timed = capture(steps_fn(args.steps))
+    if g_warm is not None:
+        time_graph(g_warm)
+    torch.cuda.synchronize()
+    ms = time_graph(g_timed)
+    ms_per_step = ms / args.steps
+    step_bytes = sum(sh.req[eff] for sh in shapes)
+    value_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    n_launch = 3 * args.steps
+    avg_launch_us = ms * 1e3 / n_launch
+    bytes_per_launch = step_bytes / 3
+    achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
+    eff_real = float(np.sum([sh.bits[eff].astype(np.int64).sum() * sh.d_out for sh in shapes]) /
+                     np.sum([sh.d_in * sh.d_out for sh in shapes]))
+    log(f"timed: {args.steps} steps in {ms:.3f} ms -> {ms_per_step * 1e3:.2f} us/step, {value_gbs:.1f} GB/s")
+
+    sweep = {}
+    if not args.no_sweep:
+        for e in effs:
+            row = {}
+            for sh in shapes:
+                def one(sh=sh, e=e):
+                    for r in range(args.sweep_reps):
+                        sh.launch(r % n_copies, e)
+                g = capture(one)
+                time_graph(g)
+                t = time_graph(g) * 1e3 / args.sweep_reps
+                gbs = sh.req[e] / (t * 1e-6) / 1e9
+                row[f"{sh.d_in}x{sh.d_out}"] = {
+                    "us": round(t, 3), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                    "eff_bits": round(float(sh.bits[e].mean()), 4), "required_MB": round(sh.req[e] / 1e6, 3)}
+            sweep[str(e) if e != 8 else "8 (dense)"] = row
+            log(f"sweep eff {e}: " + ", ".join(f"{k} {v['us']} us {v['GB/s']} GB/s" for k, v in row.items()))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(shapes, eff, args.cpu_seconds)
+        log(f"cpu baseline: {cpu}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": ("8B-shaped decode linears 4096->4096, 4096->14336, 14336->4096; b_max 8; "
+                         f"~{eff} eff. bits; batch 1; bf16 x ~ t(3), bf16 y; fp16 per-output s, z"),
+            "global_batch": 1,
+            "seq_len": 1,
+            "eff_bits_realized": round(eff_real, 4),
+            "weight_copies": n_copies,
+            "required_bytes_per_step": int(step_bytes),
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "grinqh_gemv",
+            "avg_launch_us": round(avg_launch_us, 3),
+            "bytes_per_launch": int(bytes_per_launch),
+        },
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,145 @@
+/*
+ * grinqh.h - C ABI of the MI355X (gfx950) decode-phase GEMV of GRINQH.
+ *
+ * Method source: the page "GRINQH: Graded Input-Based Quantization Hierarchy
+ * for Efficient LLM Generation" (papernotes.org note on arXiv 2606.23419),
+ * section 方法详解 / 关键设计 (key design) items 1-3, cited below as KD1
+ * (bit assignment), KD2 (bit-planar storage) and KD3 (midpoint dequant).
+ *
+ * What the library computes, for one decode step (batch 1) of one linear:
+ *
+ *   b_i = 2 * #{k : theta_k <= |x_i|}                  KD1  (P = b_max/2 thresholds)
+ *   w_hat_ij = s_j * (((q_ji >> k_i) << k_i) + phi_i) + z_j,
+ *              k_i = b_max - b_i, phi_i = 2^(k_i - 1)   KD3  (phi = 1/2 at k_i = 0)
+ *   y_j = sum over i with b_i > 0 of x_i * w_hat_ij      (channels with b_i = 0 are
+ *                                                         never read, KD1/KD2)
+ *
+ * Only the top b_i/2 two-bit planes of each loaded channel are read (KD2).
+ *
+ * Packed layout (KD2).  planes is uint32 [d_in][P][W_row], W_row =
+ * ceil(d_out/64)*4 words: for input channel i, plane p (p = 0 holds bits
+ * [b_max-2, b_max-1] of the code, the most significant), the d_out fragments
+ * are contiguous, 16 per word; the fragment of output 16w+t sits at bits
+ * [2t, 2t+1] of word w.  Rows are padded to a multiple of 64 outputs with
+ * zero fragments, so every plane row is a multiple of 16 bytes.
+ *
+ * Conventions shared by every call:
+ *  - Every pointer argument is a device pointer unless marked "host".  The
+ *    caller allocates and owns all memory; the library allocates nothing and
+ *    keeps no state beyond a cached device-property query.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and never synchronise the host.  They are thread-safe; calls
+ *    that share a workspace must be ordered on one stream.
+ *  - Arguments are checked on the host before anything touches the device;
+ *    a failed check returns an error code and launches nothing.  Nothing
+ *    throws across the ABI.  Values inside device buffers are not checked:
+ *    NaN activations get 0 bits (the channel is skipped), +-Inf gets b_max
+ *    bits and makes y non-finite, codes above 2^b_max - 1 are masked by
+ *    grinqh_pack, unsorted thresholds are used through the count formula.
+ */
+#ifndef GRINQH_H
+#define GRINQH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GRINQH_OK = 0,
+    GRINQH_EINVAL = 1,    /* NULL pointer, bad size, bad b_max, bad dtype, bad layout */
+    GRINQH_EALIGN = 2,    /* a pointer is not aligned as documented */
+    GRINQH_ENOSPACE = 3,  /* workspace smaller than grinqh_gemv_workspace_bytes() */
+    GRINQH_ENODEV = 4,    /* no HIP device is visible */
+    GRINQH_EDEVICE = 5    /* the HIP runtime reported an error (query or launch) */
+} grinqh_status;
+
+typedef enum {
+    GRINQH_BF16 = 0,      /* bfloat16, 2 bytes, 2-byte aligned */
+    GRINQH_F32 = 1        /* IEEE binary32, 4 bytes, 4-byte aligned */
+} grinqh_dtype;
+
+/* Shape of one packed linear layer (plain data; fill with grinqh_layout_init). */
+typedef struct {
+    int32_t d_in;         /* input channels (reduction dimension), 1 .. 2^20 */
+    int32_t d_out;        /* output channels, 1 .. 2^20 */
+    int32_t b_max;        /* 2, 4, 6 or 8: full code width */
+    int32_t n_planes;     /* b_max / 2 */
+    int32_t row_words;    /* ceil(d_out / 64) * 4 uint32 words per plane row */
+} grinqh_layout;
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t grinqh_version(void);
+
+/* Short constant English text for a status code (host pointer, never NULL). */
+const char* grinqh_status_string(grinqh_status status);
+
+/* Fill *out (host pointer) for a layer.  EINVAL if out is NULL, a size is
+ * outside 1 .. 2^20 or b_max is not 2, 4, 6 or 8.  Pure host function. */
+grinqh_status grinqh_layout_init(int32_t d_in, int32_t d_out, int32_t b_max,
+                                 grinqh_layout* out);
+
+/* Bytes of the packed planes: d_in * n_planes * row_words * 4 (KD2: storage
+ * stays at b_max bits per weight).  0 if L is NULL or invalid.  Host only. */
+size_t grinqh_packed_bytes(const grinqh_layout* L);
+
+/* Bytes of device workspace grinqh_gemv needs for this layout on the current
+ * device (0 if L is NULL or invalid, or no device is visible).  Host only. */
+size_t grinqh_gemv_workspace_bytes(const grinqh_layout* L);
+
+/* Offline bit-plane packing (KD2).
+ *   q       uint8 [d_out][d_in], row-major (nn.Linear orientation: q[j][i]
+ *           is the code of output j, input i); codes are masked to b_max bits.
+ *   planes  uint32 [d_in][n_planes][row_words], 16-byte aligned,
+ *           grinqh_packed_bytes(L) bytes; fully overwritten, padding included.
+ * q and planes must not overlap. */
+grinqh_status grinqh_pack(const grinqh_layout* L, const uint8_t* q, uint32_t* planes,
+                          void* stream);
+
+/* Runtime bit assignment (KD1), on its own (grinqh_gemv does the same work
+ * inside its own kernel and does not need this call).
+ *   x           [d_in] of x_dtype.
+ *   theta       float [n_planes], theta_1 .. theta_P (ascending for the
+ *               interval reading; any order is defined by the count formula).
+ *   bits        uint8 [d_in] out: b_i in {0, 2, .., b_max}.
+ *   active_idx  int32 [d_in] out or NULL: the n_active indices with b_i > 0,
+ *               ascending, in entries 0 .. n_active-1; later entries unwritten.
+ *   n_active    int32 [1] out or NULL. */
+grinqh_status grinqh_assign_bits(const grinqh_layout* L, const void* x, grinqh_dtype x_dtype,
+                                 const float* theta, uint8_t* bits, int32_t* active_idx,
+                                 int32_t* n_active, void* stream);
+
+/* The decode GEMV: bit assignment, prefix-plane streaming, midpoint dequant
+ * and the product, all in the library's kernels (KD1, KD2, KD3).
+ *   x          [d_in] of x_dtype (GRINQH_BF16 or GRINQH_F32).
+ *   theta      float [n_planes].
+ *   planes     as written by grinqh_pack, 16-byte aligned.
+ *   s, z       fp16 bit patterns [d_out]: per-output-channel scale and zero point.
+ *   y          [d_out] of y_dtype, overwritten (not accumulated); bf16 output
+ *              is the fp32 result rounded to nearest even.
+ *   workspace  >= grinqh_gemv_workspace_bytes(L) bytes, 256-byte aligned.  It
+ *              must be zero-filled before its first use; every call leaves it
+ *              ready for the next call (no clearing between calls).  Calls
+ *              sharing one workspace must not overlap in time.
+ * x and y must not overlap.  Accumulation is fp32 in a fixed order, so
+ * repeated calls on the same inputs give bit-identical y. */
+grinqh_status grinqh_gemv(const grinqh_layout* L, const void* x, grinqh_dtype x_dtype,
+                          const float* theta, const uint32_t* planes, const uint16_t* s,
+                          const uint16_t* z, void* y, grinqh_dtype y_dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Test and diagnostic call: the truncated codes q_b * 2^(b_max - b_i)
+ * (KD3's spliced truncated integer, at full scale) that the GEMV kernel's own
+ * plane decoder produces for every loaded channel, 0 for skipped channels.
+ *   bits    uint8 [d_in], as written by grinqh_assign_bits.
+ *   codes   uint8 [d_in][d_out] out. */
+grinqh_status grinqh_debug_codes(const grinqh_layout* L, const uint8_t* bits,
+                                 const uint32_t* planes, uint8_t* codes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRINQH_H */

@@ -1,0 +1,48 @@
+// Test and diagnostic kernel: the truncated codes q_b * 2^(b_max-b) that the
+// GEMV's plane decoder (decode.hpp) produces, for every loaded channel
+// (GRINQH note, key designs 2-3); skipped channels get 0.
+#include "decode.hpp"
+#include "internal.h"
+
+namespace grinqh {
+namespace {
+
+template <int P>
+__global__ __launch_bounds__(256) void debug_codes_kernel(const uint8_t* __restrict__ bits,
+                                                          const uint32_t* __restrict__ planes,
+                                                          uint8_t* __restrict__ codes, int d_in,
+                                                          int d_out, int row_words) {
+    const int w = blockIdx.x * blockDim.x + threadIdx.x;   // word within the row
+    if (w >= row_words) return;
+    for (int i = blockIdx.y; i < d_in; i += gridDim.y) {
+    const int Pi = bits[i] >> 1;
+    uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+        if (p < Pi) words[p] = planes[(static_cast<size_t>(i) * P + p) * row_words + w];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const int j = 16 * w + t;
+        if (j < d_out)
+            codes[static_cast<size_t>(i) * d_out + j] = static_cast<uint8_t>(truncated_code<P>(words, Pi, t));
+    }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_debug_codes(const grinqh_layout& L, const uint8_t* bits,
+                              const uint32_t* planes, uint8_t* codes, hipStream_t stream) {
+    dim3 block(256);
+    dim3 grid(static_cast<unsigned>((L.row_words + 255) / 256), static_cast<unsigned>(L.d_in < 65535 ? L.d_in : 65535));
+    switch (L.n_planes) {
+        case 1: debug_codes_kernel<1><<<grid, block, 0, stream>>>(bits, planes, codes, L.d_in, L.d_out, L.row_words); break;
+        case 2: debug_codes_kernel<2><<<grid, block, 0, stream>>>(bits, planes, codes, L.d_in, L.d_out, L.row_words); break;
+        case 3: debug_codes_kernel<3><<<grid, block, 0, stream>>>(bits, planes, codes, L.d_in, L.d_out, L.row_words); break;
+        case 4: debug_codes_kernel<4><<<grid, block, 0, stream>>>(bits, planes, codes, L.d_in, L.d_out, L.row_words); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace grinqh

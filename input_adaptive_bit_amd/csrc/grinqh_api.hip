@@ -1,0 +1,180 @@
+// C ABI of the GRINQH decode GEMV: argument checks, device query, dispatch.
+//
+// Every check runs on the host before any HIP call, so a rejected call
+// touches neither the device nor the stream.
+#include <atomic>
+#include <mutex>
+
+#include "internal.h"
+
+namespace grinqh {
+namespace {
+
+constexpr int kMaxDim = 1 << 20;
+constexpr int kMaxDevices = 64;
+
+std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not queried yet
+
+bool valid_layout(const grinqh_layout* L) {
+    if (L == nullptr) return false;
+    if (L->d_in < 1 || L->d_in > kMaxDim || L->d_out < 1 || L->d_out > kMaxDim) return false;
+    if (L->b_max != 2 && L->b_max != 4 && L->b_max != 6 && L->b_max != 8) return false;
+    if (L->n_planes != L->b_max / 2) return false;
+    if (L->row_words != ((L->d_out + 63) / 64) * 4) return false;
+    return true;
+}
+
+bool valid_dtype(int d) { return d == GRINQH_BF16 || d == GRINQH_F32; }
+
+int dtype_bytes(int d) { return d == GRINQH_BF16 ? 2 : 4; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+grinqh_status map_error(hipError_t e) {
+    if (e == hipSuccess) return GRINQH_OK;
+    if (e == hipErrorNoDevice || e == hipErrorInvalidDevice) return GRINQH_ENODEV;
+    return GRINQH_EDEVICE;
+}
+
+}  // namespace
+
+bool current_device_info(DeviceInfo* out, hipError_t* err) {
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || n <= 0) {
+        *err = (e == hipSuccess) ? hipErrorNoDevice : e;
+        return false;
+    }
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *err = e;
+        return false;
+    }
+    int cu = (dev >= 0 && dev < kMaxDevices) ? g_cu_count[dev].load(std::memory_order_relaxed) : 0;
+    if (cu == 0) {
+        e = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || cu <= 0) {
+            *err = (e == hipSuccess) ? hipErrorInvalidDevice : e;
+            return false;
+        }
+        if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(cu, std::memory_order_relaxed);
+    }
+    out->device = dev;
+    out->cu_count = cu;
+    *err = hipSuccess;
+    return true;
+}
+
+}  // namespace grinqh
+
+using namespace grinqh;
+
+extern "C" {
+
+int32_t grinqh_version(void) { return 100; }
+
+const char* grinqh_status_string(grinqh_status status) {
+    switch (status) {
+        case GRINQH_OK: return "ok";
+        case GRINQH_EINVAL: return "invalid argument";
+        case GRINQH_EALIGN: return "misaligned pointer";
+        case GRINQH_ENOSPACE: return "workspace too small";
+        case GRINQH_ENODEV: return "no HIP device";
+        case GRINQH_EDEVICE: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+grinqh_status grinqh_layout_init(int32_t d_in, int32_t d_out, int32_t b_max, grinqh_layout* out) {
+    if (out == nullptr) return GRINQH_EINVAL;
+    if (d_in < 1 || d_in > kMaxDim || d_out < 1 || d_out > kMaxDim) return GRINQH_EINVAL;
+    if (b_max != 2 && b_max != 4 && b_max != 6 && b_max != 8) return GRINQH_EINVAL;
+    out->d_in = d_in;
+    out->d_out = d_out;
+    out->b_max = b_max;
+    out->n_planes = b_max / 2;
+    out->row_words = ((d_out + 63) / 64) * 4;
+    return GRINQH_OK;
+}
+
+size_t grinqh_packed_bytes(const grinqh_layout* L) {
+    if (!valid_layout(L)) return 0;
+    return static_cast<size_t>(L->d_in) * L->n_planes * L->row_words * 4u;
+}
+
+size_t grinqh_gemv_workspace_bytes(const grinqh_layout* L) {
+    if (!valid_layout(L)) return 0;
+    DeviceInfo dev;
+    hipError_t e;
+    if (!current_device_info(&dev, &e)) return 0;
+    return plan_gemv(*L, dev).ws_bytes;
+}
+
+grinqh_status grinqh_pack(const grinqh_layout* L, const uint8_t* q, uint32_t* planes,
+                          void* stream) {
+    if (!valid_layout(L) || q == nullptr || planes == nullptr) return GRINQH_EINVAL;
+    if (!aligned(planes, 16)) return GRINQH_EALIGN;
+    DeviceInfo dev;
+    hipError_t e;
+    if (!current_device_info(&dev, &e)) return map_error(e);
+    return map_error(launch_pack(*L, q, planes, static_cast<hipStream_t>(stream)));
+}
+
+grinqh_status grinqh_assign_bits(const grinqh_layout* L, const void* x, grinqh_dtype x_dtype,
+                                 const float* theta, uint8_t* bits, int32_t* active_idx,
+                                 int32_t* n_active, void* stream) {
+    if (!valid_layout(L) || x == nullptr || theta == nullptr || bits == nullptr)
+        return GRINQH_EINVAL;
+    if (!valid_dtype(x_dtype)) return GRINQH_EINVAL;
+    if (!aligned(x, dtype_bytes(x_dtype)) || !aligned(theta, 4)) return GRINQH_EALIGN;
+    if ((active_idx && !aligned(active_idx, 4)) || (n_active && !aligned(n_active, 4)))
+        return GRINQH_EALIGN;
+    DeviceInfo dev;
+    hipError_t e;
+    if (!current_device_info(&dev, &e)) return map_error(e);
+    return map_error(launch_assign_bits(*L, x, x_dtype, theta, bits, active_idx, n_active,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+grinqh_status grinqh_gemv(const grinqh_layout* L, const void* x, grinqh_dtype x_dtype,
+                          const float* theta, const uint32_t* planes, const uint16_t* s,
+                          const uint16_t* z, void* y, grinqh_dtype y_dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (!valid_layout(L) || x == nullptr || theta == nullptr || planes == nullptr ||
+        s == nullptr || z == nullptr || y == nullptr || workspace == nullptr)
+        return GRINQH_EINVAL;
+    if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return GRINQH_EINVAL;
+    if (!aligned(x, dtype_bytes(x_dtype)) || !aligned(y, dtype_bytes(y_dtype)) ||
+        !aligned(theta, 4) || !aligned(planes, 16) || !aligned(s, 2) || !aligned(z, 2) ||
+        !aligned(workspace, 256))
+        return GRINQH_EALIGN;
+    {
+        // x and y must not overlap
+        uintptr_t xb = reinterpret_cast<uintptr_t>(x);
+        uintptr_t xe = xb + static_cast<size_t>(L->d_in) * dtype_bytes(x_dtype);
+        uintptr_t yb = reinterpret_cast<uintptr_t>(y);
+        uintptr_t ye = yb + static_cast<size_t>(L->d_out) * dtype_bytes(y_dtype);
+        if (xb < ye && yb < xe) return GRINQH_EINVAL;
+    }
+    DeviceInfo dev;
+    hipError_t e;
+    if (!current_device_info(&dev, &e)) return map_error(e);
+    GemvPlan plan = plan_gemv(*L, dev);
+    if (workspace_bytes < plan.ws_bytes) return GRINQH_ENOSPACE;
+    return map_error(launch_gemv(*L, plan, x, x_dtype, theta, planes, s, z, y, y_dtype,
+                                 workspace, static_cast<hipStream_t>(stream)));
+}
+
+grinqh_status grinqh_debug_codes(const grinqh_layout* L, const uint8_t* bits,
+                                 const uint32_t* planes, uint8_t* codes, void* stream) {
+    if (!valid_layout(L) || bits == nullptr || planes == nullptr || codes == nullptr)
+        return GRINQH_EINVAL;
+    if (!aligned(planes, 16)) return GRINQH_EALIGN;
+    DeviceInfo dev;
+    hipError_t e;
+    if (!current_device_info(&dev, &e)) return map_error(e);
+    return map_error(launch_debug_codes(*L, bits, planes, codes, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

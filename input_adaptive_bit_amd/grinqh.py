@@ -1,0 +1,241 @@
+"""Python binding of libgrinqh.so (the C ABI in include/grinqh.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libgrinqh.so.  PyTorch supplies device memory and the stream.
+The functions with the C names take a grinqh_layout and caller-allocated
+tensors, exactly like the C calls; the short names (pack, assign_bits, gemv,
+debug_codes) allocate their outputs with torch and call the same entry points.
+There is no CPU fallback: a missing library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgrinqh.so")
+
+GRINQH_OK, GRINQH_EINVAL, GRINQH_EALIGN, GRINQH_ENOSPACE, GRINQH_ENODEV, GRINQH_EDEVICE = range(6)
+GRINQH_BF16, GRINQH_F32 = 0, 1
+
+
+class GrinqhError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {status_string(status)} (status {status})")
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32), ("b_max", ctypes.c_int32),
+                ("n_planes", ctypes.c_int32), ("row_words", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"Layout(d_in={self.d_in}, d_out={self.d_out}, b_max={self.b_max}, "
+                f"n_planes={self.n_planes}, row_words={self.row_words})")
+
+
+EXPORTS = ("grinqh_version", "grinqh_status_string", "grinqh_layout_init", "grinqh_packed_bytes",
+           "grinqh_gemv_workspace_bytes", "grinqh_pack", "grinqh_assign_bits", "grinqh_gemv",
+           "grinqh_debug_codes")
+
+_lib = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libgrinqh.so (built in-tree by input_adaptive_bit_amd.build)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    # Bind to the HIP runtime torch already uses (same soname), so that streams
+    # and device pointers handed over by torch belong to the runtime we call.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m input_adaptive_bit_amd.build` "
+                           "(there is no CPU fallback)")
+    lib = ctypes.CDLL(p)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    LP = ctypes.POINTER(Layout)
+    lib.grinqh_version.argtypes = []
+    lib.grinqh_version.restype = i32
+    lib.grinqh_status_string.argtypes = [ctypes.c_int]
+    lib.grinqh_status_string.restype = ctypes.c_char_p
+    lib.grinqh_layout_init.argtypes = [i32, i32, i32, LP]
+    lib.grinqh_layout_init.restype = ctypes.c_int
+    lib.grinqh_packed_bytes.argtypes = [LP]
+    lib.grinqh_packed_bytes.restype = sz
+    lib.grinqh_gemv_workspace_bytes.argtypes = [LP]
+    lib.grinqh_gemv_workspace_bytes.restype = sz
+    lib.grinqh_pack.argtypes = [LP, vp, vp, vp]
+    lib.grinqh_pack.restype = ctypes.c_int
+    lib.grinqh_assign_bits.argtypes = [LP, vp, ctypes.c_int, vp, vp, vp, vp, vp]
+    lib.grinqh_assign_bits.restype = ctypes.c_int
+    lib.grinqh_gemv.argtypes = [LP, vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
+    lib.grinqh_gemv.restype = ctypes.c_int
+    lib.grinqh_debug_codes.argtypes = [LP, vp, vp, vp, vp]
+    lib.grinqh_debug_codes.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().grinqh_status_string(int(status)).decode()
+
+
+def _check(status: int, call: str) -> None:
+    if status != GRINQH_OK:
+        raise GrinqhError(status, call)
+
+
+# ------------------------------------------------------------------ host ----
+
+def grinqh_layout_init(d_in: int, d_out: int, b_max: int) -> Layout:
+    L = Layout()
+    _check(load().grinqh_layout_init(int(d_in), int(d_out), int(b_max), ctypes.byref(L)),
+           "grinqh_layout_init")
+    return L
+
+
+def grinqh_packed_bytes(L: Layout) -> int:
+    return int(load().grinqh_packed_bytes(ctypes.byref(L)))
+
+
+def grinqh_gemv_workspace_bytes(L: Layout) -> int:
+    return int(load().grinqh_gemv_workspace_bytes(ctypes.byref(L)))
+
+
+# --------------------------------------------------------------- device -----
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GRINQH_BF16
+    if t.dtype == torch.float32:
+        return GRINQH_F32
+    raise TypeError(f"x/y must be bfloat16 or float32, not {t.dtype}")
+
+
+def _need(t, name, dtypes, numel=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if numel is not None and t.numel() * t.element_size() < numel:
+        raise ValueError(f"{name} is too small ({t.numel() * t.element_size()} < {numel} bytes)")
+
+
+def grinqh_pack(L: Layout, q, planes, stream=None) -> None:
+    import torch
+    _need(q, "q", (torch.uint8,), L.d_out * L.d_in)
+    _need(planes, "planes", (torch.int32, torch.uint32), grinqh_packed_bytes(L))
+    _check(load().grinqh_pack(ctypes.byref(L), _ptr(q), _ptr(planes), _stream(stream)), "grinqh_pack")
+
+
+def grinqh_assign_bits(L: Layout, x, theta, bits, active_idx=None, n_active=None, stream=None) -> None:
+    import torch
+    _need(x, "x", (torch.bfloat16, torch.float32), L.d_in * x.element_size())
+    _need(theta, "theta", (torch.float32,), 4 * L.n_planes)
+    _need(bits, "bits", (torch.uint8,), L.d_in)
+    if active_idx is not None:
+        _need(active_idx, "active_idx", (torch.int32,), 4 * L.d_in)
+    if n_active is not None:
+        _need(n_active, "n_active", (torch.int32,), 4)
+    _check(load().grinqh_assign_bits(ctypes.byref(L), _ptr(x), _dtype_code(x), _ptr(theta), _ptr(bits),
+                                     _ptr(active_idx), _ptr(n_active), _stream(stream)),
+           "grinqh_assign_bits")
+
+
+def grinqh_gemv(L: Layout, x, theta, planes, s, z, y, workspace, stream=None) -> None:
+    import torch
+    _need(x, "x", (torch.bfloat16, torch.float32), L.d_in * x.element_size())
+    _need(theta, "theta", (torch.float32,), 4 * L.n_planes)
+    _need(planes, "planes", (torch.int32, torch.uint32), grinqh_packed_bytes(L))
+    _need(s, "s", (torch.float16,), 2 * L.d_out)
+    _need(z, "z", (torch.float16,), 2 * L.d_out)
+    _need(y, "y", (torch.bfloat16, torch.float32), L.d_out * y.element_size())
+    _need(workspace, "workspace", None)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().grinqh_gemv(ctypes.byref(L), _ptr(x), _dtype_code(x), _ptr(theta), _ptr(planes),
+                              _ptr(s), _ptr(z), _ptr(y), _dtype_code(y), _ptr(workspace), ws_bytes,
+                              _stream(stream)),
+           "grinqh_gemv")
+
+
+def grinqh_debug_codes(L: Layout, bits, planes, codes, stream=None) -> None:
+    import torch
+    _need(bits, "bits", (torch.uint8,), L.d_in)
+    _need(planes, "planes", (torch.int32, torch.uint32), grinqh_packed_bytes(L))
+    _need(codes, "codes", (torch.uint8,), L.d_in * L.d_out)
+    _check(load().grinqh_debug_codes(ctypes.byref(L), _ptr(bits), _ptr(planes), _ptr(codes),
+                                     _stream(stream)),
+           "grinqh_debug_codes")
+
+
+# ------------------------------------------------- allocating conveniences --
+
+def new_workspace(L: Layout, device=None):
+    """A zero-filled workspace tensor for grinqh_gemv on `device`."""
+    import torch
+    n = grinqh_gemv_workspace_bytes(L)
+    if n == 0:
+        raise GrinqhError(GRINQH_ENODEV, "grinqh_gemv_workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def pack(q, b_max: int, stream=None):
+    """q uint8 [d_out][d_in] (cuda) -> (layout, planes int32 [d_in][P][W_row])."""
+    import torch
+    d_out, d_in = q.shape
+    L = grinqh_layout_init(d_in, d_out, b_max)
+    planes = torch.empty((d_in, L.n_planes, L.row_words), dtype=torch.int32, device=q.device)
+    grinqh_pack(L, q, planes, stream)
+    return L, planes
+
+
+def assign_bits(L: Layout, x, theta, stream=None) -> Tuple:
+    import torch
+    bits = torch.empty(L.d_in, dtype=torch.uint8, device=x.device)
+    idx = torch.empty(L.d_in, dtype=torch.int32, device=x.device)
+    n = torch.empty(1, dtype=torch.int32, device=x.device)
+    grinqh_assign_bits(L, x, theta, bits, idx, n, stream)
+    return bits, idx, n
+
+
+def gemv(L: Layout, x, theta, planes, s, z, workspace=None, out_dtype=None, stream=None):
+    import torch
+    if workspace is None:
+        workspace = new_workspace(L, x.device)
+    y = torch.empty(L.d_out, dtype=out_dtype or torch.float32, device=x.device)
+    grinqh_gemv(L, x, theta, planes, s, z, y, workspace, stream)
+    return y
+
+
+def debug_codes(L: Layout, bits, planes, stream=None):
+    import torch
+    codes = torch.empty((L.d_in, L.d_out), dtype=torch.uint8, device=bits.device)
+    grinqh_debug_codes(L, bits, planes, codes, stream)
+    return codes

@@ -1,0 +1,128 @@
+"""Host-side tests of libgrinqh.so that need no GPU.
+
+They check that the library loads, that it exports every function
+include/grinqh.h declares, the pure-host layout arithmetic, and that argument
+checks reject bad calls with the documented status before touching a device
+(every call here fails a host check, so no kernel is ever launched).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import input_adaptive_bit_amd as G
+from input_adaptive_bit_amd import grinqh as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "grinqh.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(grinqh_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_function():
+    lib = G.load()
+    declared = _declared_functions()
+    assert declared, "no declarations parsed"
+    assert set(declared) == set(B.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (grinqh_[a-z_]+)\b", out))
+    assert set(declared) <= exported
+
+
+def test_library_has_gfx950_code_object():
+    """The library built here carries a gfx950 device code object."""
+    with open(B.LIB_PATH, "rb") as f:
+        blob = f.read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_version_and_status_strings():
+    assert G.load().grinqh_version() >= 100
+    for st in range(6):
+        assert isinstance(G.status_string(st), str) and G.status_string(st)
+
+
+@pytest.mark.parametrize("d_in,d_out,b_max,words", [(1024, 1024, 8, 64), (4096, 14336, 8, 896),
+                                                   (7, 1, 4, 4), (3, 65, 2, 8), (5, 128, 6, 8)])
+def test_layout_init_and_packed_bytes(d_in, d_out, b_max, words):
+    L = G.grinqh_layout_init(d_in, d_out, b_max)
+    assert (L.d_in, L.d_out, L.b_max, L.n_planes, L.row_words) == (d_in, d_out, b_max, b_max // 2, words)
+    assert G.grinqh_packed_bytes(L) == d_in * (b_max // 2) * words * 4
+
+
+@pytest.mark.parametrize("d_in,d_out,b_max", [(0, 10, 8), (10, 0, 8), (10, 10, 3), (10, 10, 10),
+                                              (10, 10, 0), ((1 << 20) + 1, 10, 8), (-4, 5, 4)])
+def test_layout_init_rejects(d_in, d_out, b_max):
+    L = B.Layout()
+    st = G.load().grinqh_layout_init(d_in, d_out, b_max, ctypes.byref(L))
+    assert st == B.GRINQH_EINVAL
+    assert G.load().grinqh_layout_init(8, 8, 8, None) == B.GRINQH_EINVAL
+
+
+def test_inconsistent_layout_is_rejected_everywhere():
+    lib = G.load()
+    L = G.grinqh_layout_init(64, 64, 8)
+    L.row_words = 5
+    assert lib.grinqh_packed_bytes(ctypes.byref(L)) == 0
+    assert lib.grinqh_gemv_workspace_bytes(ctypes.byref(L)) == 0
+    p = 4096
+    assert lib.grinqh_pack(ctypes.byref(L), p, p, None) == B.GRINQH_EINVAL
+    assert lib.grinqh_gemv(ctypes.byref(L), p, 0, p, p, p, p, p + 100000, 1, p * 4, 1 << 20, None) \
+        == B.GRINQH_EINVAL
+
+
+def test_argument_checks_before_any_device_call():
+    """Fake (never dereferenced) addresses: every call below fails a host check."""
+    lib = G.load()
+    L = G.grinqh_layout_init(256, 128, 8)
+    Lp = ctypes.byref(L)
+    A = 1 << 16          # 64 KiB-aligned fake addresses
+    X, TH, PL, S, Z, Y, WS = (A * k for k in range(1, 8))
+    ok = lambda **kw: dict(dict(x=X, xd=0, th=TH, pl=PL, s=S, z=Z, y=Y, yd=1, ws=WS, wsb=1 << 30), **kw)
+
+    def gemv(a):
+        return lib.grinqh_gemv(Lp, a["x"], a["xd"], a["th"], a["pl"], a["s"], a["z"], a["y"], a["yd"],
+                               a["ws"], a["wsb"], None)
+
+    for key in ("x", "th", "pl", "s", "z", "y", "ws"):
+        assert gemv(ok(**{key: None})) == B.GRINQH_EINVAL, key
+    assert gemv(ok(xd=7)) == B.GRINQH_EINVAL
+    assert gemv(ok(yd=-1)) == B.GRINQH_EINVAL
+    assert gemv(ok(pl=PL + 4)) == B.GRINQH_EALIGN
+    assert gemv(ok(x=X + 1)) == B.GRINQH_EALIGN
+    assert gemv(ok(xd=1, x=X + 2)) == B.GRINQH_EALIGN
+    assert gemv(ok(y=Y + 2)) == B.GRINQH_EALIGN
+    assert gemv(ok(s=S + 1)) == B.GRINQH_EALIGN
+    assert gemv(ok(ws=WS + 16)) == B.GRINQH_EALIGN
+    assert gemv(ok(th=TH + 2)) == B.GRINQH_EALIGN
+    assert gemv(ok(y=X + 128)) == B.GRINQH_EINVAL          # y overlaps x
+    assert lib.grinqh_gemv(None, X, 0, TH, PL, S, Z, Y, 1, WS, 1 << 30, None) == B.GRINQH_EINVAL
+
+    assert lib.grinqh_pack(Lp, None, PL, None) == B.GRINQH_EINVAL
+    assert lib.grinqh_pack(Lp, X, None, None) == B.GRINQH_EINVAL
+    assert lib.grinqh_pack(Lp, X, PL + 8, None) == B.GRINQH_EALIGN
+
+    assert lib.grinqh_assign_bits(Lp, None, 0, TH, Y, None, None, None) == B.GRINQH_EINVAL
+    assert lib.grinqh_assign_bits(Lp, X, 0, None, Y, None, None, None) == B.GRINQH_EINVAL
+    assert lib.grinqh_assign_bits(Lp, X, 0, TH, None, None, None, None) == B.GRINQH_EINVAL
+    assert lib.grinqh_assign_bits(Lp, X, 5, TH, Y, None, None, None) == B.GRINQH_EINVAL
+    assert lib.grinqh_assign_bits(Lp, X + 1, 0, TH, Y, None, None, None) == B.GRINQH_EALIGN
+    assert lib.grinqh_assign_bits(Lp, X, 0, TH, Y, S + 2, None, None) == B.GRINQH_EALIGN
+
+    assert lib.grinqh_debug_codes(Lp, None, PL, Y, None) == B.GRINQH_EINVAL
+    assert lib.grinqh_debug_codes(Lp, X, PL + 4, Y, None) == B.GRINQH_EALIGN
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        B.load(str(tmp_path / "missing.so"))

@@ -1,0 +1,341 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bit-exact: packed planes, b_i, the ascending active list and its length,
+the decoded codes.  Within tolerance (max relative error, denominator
+max(|y*_j|, 1e-2 * rms(y*))): fp32 y <= 2e-3; bf16 y <= 2e-3 + 2^-8 and equal
+to the fp32 result rounded to nearest even.  Oracle inputs are the seeded
+synthetic arrays; no expected value comes from the HIP path.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import grinqh_oracle as O
+from oracle import c_oracle as C
+import synthetic as S
+from tests.gpu_util import TOL_BF16, TOL_F32, DeviceLinear, require_gpu, say, to_dev, to_dev_x
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import input_adaptive_bit_amd as G
+    G.load()
+    return require_gpu()
+
+
+def _theta_dev(theta, dev):
+    return to_dev(np.asarray(theta, np.float32), dev)
+
+
+def _check_y(y_dev, y_ref, tol, what):
+    import torch
+    y = y_dev.float().cpu().numpy().astype(np.float64)
+    err = O.max_rel_error(y, y_ref)
+    say(f"  {what}: max rel err {err:.3e}")
+    assert err <= tol, f"{what}: max rel err {err:.3e} > {tol:.3e}"
+    return y
+
+
+def _run_and_check(dl, x_f32, x_dtype, theta, y_ref, what, dev, check_bf16=True):
+    import torch
+    xd = to_dev_x(x_f32, x_dtype, dev)
+    td = _theta_dev(theta, dev)
+    y32 = dl.gemv(xd, td, torch.float32)
+    y32b = dl.gemv(xd, td, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y32.view(torch.int32), y32b.view(torch.int32)), f"{what}: not deterministic"
+    y = _check_y(y32, y_ref, TOL_F32, what + " fp32")
+    if check_bf16:
+        yb = dl.gemv(xd, td, torch.bfloat16)
+        torch.cuda.synchronize()
+        _check_y(yb, y_ref, TOL_BF16, what + " bf16")
+        rne = O.round_to_bf16(y.astype(np.float32))
+        got = yb.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, rne), f"{what}: bf16 output is not RNE of the fp32 output"
+    return y
+
+
+# ------------------------------------------------------------- packing ------
+
+@pytest.mark.parametrize("b_max", [2, 4, 6, 8])
+@pytest.mark.parametrize("d_in,d_out", [(1, 1), (5, 1), (3, 65), (70, 130), (257, 1000), (1024, 1024),
+                                        (65, 64)])
+def test_pack_bit_exact(dev, b_max, d_in, d_out):
+    say(f"pack b_max={b_max} d_in={d_in} d_out={d_out}")
+    rng = np.random.default_rng(d_in * 7919 + d_out * 31 + b_max)
+    q = rng.integers(0, 256, size=(d_out, d_in), dtype=np.uint8)    # high bits must be masked
+    dl = DeviceLinear(q, np.ones(d_out, np.float16), np.zeros(d_out, np.float16), b_max, dev)
+    assert np.array_equal(dl.planes_np(), C.pack_planes(q, b_max))
+
+
+# ------------------------------------------------------ bit assignment ------
+
+def _assign_check(x_f32, x_dtype, theta, b_max, dev, what):
+    import torch
+    import input_adaptive_bit_amd as G
+    say(f"assign {what}")
+    x_f32 = np.asarray(x_f32, np.float32)
+    L = G.grinqh_layout_init(x_f32.size, 64, b_max)
+    bits, idx, n = G.assign_bits(L, to_dev_x(x_f32, x_dtype, dev), _theta_dev(theta, dev))
+    torch.cuda.synchronize()
+    x_seen = x_f32 if x_dtype == "f32" else S.bf16_bits_to_f32(S.f32_to_bf16_bits(x_f32))
+    ref = O.assign_bits(x_seen, theta, b_max)
+    got = bits.cpu().numpy()
+    assert np.array_equal(got, ref)
+    act = O.active_channels(ref)
+    n_got = int(n.cpu().item())
+    assert n_got == act.size
+    assert np.array_equal(idx.cpu().numpy()[:n_got], act)
+
+
+def test_assign_small_case(dev):
+    L = S.make_linear(S.small_case(), with_codes=False)
+    _assign_check(L.x, "f32", L.theta, 8, dev, "small case fp32")
+
+
+@pytest.mark.parametrize("d_in", [1, 63, 64, 1025, 3000, 14336])
+@pytest.mark.parametrize("b_max", [2, 4, 8])
+def test_assign_bf16_ragged(dev, d_in, b_max):
+    rng = np.random.default_rng(d_in + b_max)
+    x = rng.standard_t(3, d_in).astype(np.float32)
+    theta = np.sort(np.quantile(np.abs(x), np.linspace(0.2, 0.9, b_max // 2))).astype(np.float32)
+    _assign_check(x, "bf16", theta, b_max, dev, f"bf16 d_in={d_in} b_max={b_max}")
+
+
+def test_assign_special_values(dev, golden_dir):
+    import json, os
+    g = json.load(open(os.path.join(golden_dir, "assign_bits_ties.json")))
+    x = np.array([float(v) for v in g["x"]], np.float32)
+    _assign_check(x, "f32", np.array(g["theta"], np.float32), 8, dev, "golden ties fp32")
+    _assign_check(x, "bf16", np.array(g["theta"], np.float32), 8, dev, "golden ties bf16")
+    z = np.zeros(100, np.float32)
+    _assign_check(z, "f32", np.zeros(4, np.float32), 8, dev, "dense zeros")
+    _assign_check(np.ones(100, np.float32), "f32", np.full(4, np.inf, np.float32), 8, dev, "all skipped")
+
+
+# ------------------------------------------------------------- codes --------
+
+@pytest.mark.parametrize("b_max", [2, 4, 6, 8])
+def test_debug_codes_bit_exact(dev, b_max):
+    import torch
+    import input_adaptive_bit_amd as G
+    say(f"debug codes b_max={b_max}")
+    rng = np.random.default_rng(50 + b_max)
+    d_in, d_out = 300, 1000
+    q = rng.integers(0, 1 << b_max, size=(d_out, d_in), dtype=np.uint8)
+    x = rng.standard_normal(d_in).astype(np.float32)
+    theta = np.sort(np.quantile(np.abs(x), np.linspace(0.15, 0.85, b_max // 2))).astype(np.float32)
+    dl = DeviceLinear(q, np.ones(d_out, np.float16), np.zeros(d_out, np.float16), b_max, dev)
+    bits, _, _ = G.assign_bits(dl.L, to_dev_x(x, "f32", dev), _theta_dev(theta, dev))
+    codes = G.debug_codes(dl.L, bits, dl.planes)
+    torch.cuda.synchronize()
+    ref_bits = O.assign_bits(x, theta, b_max)
+    ref = O.truncated_codes(q, ref_bits, b_max)
+    assert np.array_equal(codes.cpu().numpy().astype(np.int64), ref)
+
+
+# -------------------------------------------------------------- GEMV --------
+
+def test_gemv_small_case(dev):
+    L = S.make_linear(S.small_case())
+    say("gemv small case 1024x1024 fp32 x")
+    dl = DeviceLinear(L.q, L.s, L.z, 8, dev)
+    y_ref = O.gemv(L.x, L.theta, L.q, L.s, L.z, 8, exact=True)
+    _run_and_check(dl, L.x, "f32", L.theta, y_ref, "small case", dev)
+
+
+@pytest.mark.parametrize("b_max", [2, 4, 6, 8])
+@pytest.mark.parametrize("d_in,d_out", [(1, 1), (1, 65), (3, 1), (17, 100), (300, 1500), (1000, 64),
+                                        (2049, 3000)])
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+def test_gemv_ragged_shapes(dev, b_max, d_in, d_out, x_dtype):
+    say(f"gemv ragged b_max={b_max} {d_in}->{d_out} x={x_dtype}")
+    rng = np.random.default_rng(d_in * 131 + d_out * 7 + b_max)
+    q = rng.integers(0, 1 << b_max, size=(d_out, d_in), dtype=np.uint8)
+    s = rng.uniform(0.001, 0.01, d_out).astype(np.float16)
+    z = rng.normal(0, 0.01, d_out).astype(np.float16)
+    x = rng.standard_t(3, d_in).astype(np.float32)
+    if x_dtype == "bf16":
+        x = S.bf16_bits_to_f32(S.f32_to_bf16_bits(x))
+    theta = np.sort(np.quantile(np.abs(x), np.linspace(0.2, 0.9, b_max // 2))).astype(np.float32)
+    dl = DeviceLinear(q, s, z, b_max, dev)
+    y_ref = C.gemv(x, theta, q, s, z, b_max)
+    _run_and_check(dl, x, x_dtype, theta, y_ref, f"{d_in}->{d_out} b{b_max}", dev)
+
+
+def test_gemv_dense_and_all_skipped(dev):
+    import torch
+    rng = np.random.default_rng(5)
+    d_in, d_out = 777, 2000
+    q = rng.integers(0, 256, size=(d_out, d_in), dtype=np.uint8)
+    s = rng.uniform(0.001, 0.01, d_out).astype(np.float16)
+    z = rng.normal(0, 0.01, d_out).astype(np.float16)
+    x = rng.standard_normal(d_in).astype(np.float32)
+    dl = DeviceLinear(q, s, z, 8, dev)
+    say("gemv dense thresholds")
+    th0 = np.zeros(4, np.float32)
+    _run_and_check(dl, x, "f32", th0, C.gemv(x, th0, q, s, z, 8), "dense", dev)
+    say("gemv all skipped")
+    for th in (np.full(4, np.inf, np.float32), np.full(4, 1e30, np.float32)):
+        y = dl.gemv(to_dev_x(x, "f32", dev), _theta_dev(th, dev), torch.float32)
+        torch.cuda.synchronize()
+        assert np.all(y.cpu().numpy() == 0.0)
+
+
+def test_gemv_single_active_channel(dev):
+    rng = np.random.default_rng(6)
+    d_in, d_out = 500, 1100
+    q = rng.integers(0, 256, size=(d_out, d_in), dtype=np.uint8)
+    s = rng.uniform(0.001, 0.01, d_out).astype(np.float16)
+    z = rng.normal(0, 0.01, d_out).astype(np.float16)
+    x = np.full(d_in, 0.01, np.float32)
+    x[321] = -3.0
+    theta = np.array([1.0, 2.0, 2.5, 9.0], np.float32)
+    dl = DeviceLinear(q, s, z, 8, dev)
+    say("gemv single active channel")
+    _run_and_check(dl, x, "f32", theta, C.gemv(x, theta, q, s, z, 8), "single channel", dev)
+
+
+def test_gemv_nan_and_inf(dev):
+    import torch
+    rng = np.random.default_rng(8)
+    d_in, d_out = 256, 256
+    q = rng.integers(0, 256, size=(d_out, d_in), dtype=np.uint8)
+    s = rng.uniform(0.001, 0.01, d_out).astype(np.float16)
+    z = rng.normal(0, 0.01, d_out).astype(np.float16)
+    x = rng.standard_normal(d_in).astype(np.float32)
+    theta = np.array([0.2, 0.5, 1.0, 2.0], np.float32)
+    dl = DeviceLinear(q, s, z, 8, dev)
+    xn = x.copy()
+    xn[7] = np.nan
+    say("gemv NaN activation")
+    _run_and_check(dl, xn, "f32", theta, C.gemv(xn, theta, q, s, z, 8), "nan channel skipped", dev)
+    xi = x.copy()
+    xi[9] = np.inf
+    y = dl.gemv(to_dev_x(xi, "f32", dev), _theta_dev(theta, dev), torch.float32)
+    torch.cuda.synchronize()
+    assert not np.all(np.isfinite(y.cpu().numpy()))
+
+
+def test_gemv_bruteforce_8x8(dev):
+    """8 channels x 8 outputs (padded to 64), b_max 8: a seeded 1000-pattern
+    subset of the 5^8 level patterns, the 5 uniform patterns and exact ties."""
+    import torch
+    rng = np.random.default_rng(88)
+    q = rng.integers(0, 256, size=(8, 8), dtype=np.uint8)
+    s = rng.uniform(0.001, 0.01, 8).astype(np.float16)
+    z = rng.normal(0, 0.01, 8).astype(np.float16)
+    theta = np.array([0.5, 1.0, 2.0, 4.0], np.float32)
+    mid = np.array([0.25, 0.75, 1.5, 3.0, 6.0], np.float32)
+    pats = [np.array(p) for p in rng.integers(0, 5, size=(1000, 8))]
+    pats += [np.full(8, L) for L in range(5)]
+    dl = DeviceLinear(q, s, z, 8, dev)
+    td = _theta_dev(theta, dev)
+    say("gemv brute force 8x8")
+    xs = []
+    for p in pats:
+        sign = np.where(rng.random(8) < 0.5, -1.0, 1.0).astype(np.float32)
+        xs.append(sign * mid[p])
+    for k in range(20):                             # exact ties |x| = theta_k
+        xs.append(rng.choice(np.concatenate([theta, -theta, [0.0]]), 8).astype(np.float32))
+    ys = [dl.gemv(to_dev_x(xv, "f32", dev), td, torch.float32) for xv in xs]
+    torch.cuda.synchronize()
+    worst = 0.0
+    for xv, yd in zip(xs, ys):
+        ref = O.gemv(xv, theta, q, s, z, 8, exact=True)
+        err = O.max_rel_error(yd.cpu().numpy(), ref) if np.any(ref != 0) else float(np.max(np.abs(yd.cpu().numpy())))
+        worst = max(worst, err)
+    say(f"  worst rel err {worst:.3e}")
+    assert worst <= TOL_F32
+
+
+def test_gemv_power_of_two_scaling_is_exact(dev):
+    import torch
+    rng = np.random.default_rng(9)
+    d_in, d_out = 1500, 2100
+    q = rng.integers(0, 256, size=(d_out, d_in), dtype=np.uint8)
+    s = rng.uniform(0.001, 0.01, d_out).astype(np.float16)
+    z = rng.normal(0, 0.01, d_out).astype(np.float16)
+    x = S.bf16_bits_to_f32(S.f32_to_bf16_bits(rng.standard_t(3, d_in).astype(np.float32)))
+    theta = np.sort(np.quantile(np.abs(x), [0.2, 0.5, 0.8, 0.95])).astype(np.float32)
+    dl = DeviceLinear(q, s, z, 8, dev)
+    say("gemv power-of-two scaling")
+    y0 = dl.gemv(to_dev_x(x, "bf16", dev), _theta_dev(theta, dev), torch.float32)
+    for m in (-4, 3):
+        ym = dl.gemv(to_dev_x(np.ldexp(x, m).astype(np.float32), "bf16", dev),
+                     _theta_dev(np.ldexp(theta, m).astype(np.float32), dev), torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(ym, y0 * (2.0 ** m))
+
+
+# ------------------------------------------------- full-size workloads ------
+
+def _full_linear_check(spec, dev, sample=None):
+    import torch
+    L = S.make_linear(spec)
+    say(f"full {spec.d_in}->{spec.d_out} b_max={spec.b_max} key={spec.key} q={spec.quantiles}")
+    dl = DeviceLinear(L.q, L.s, L.z, spec.b_max, dev)
+    xd = to_dev_x(L.x, spec.x_dtype, dev)
+    y = dl.gemv(xd, _theta_dev(L.theta, dev), torch.float32)
+    yb = dl.gemv(xd, _theta_dev(L.theta, dev), torch.bfloat16)
+    torch.cuda.synchronize()
+    cols = np.arange(spec.d_out) if sample is None else sample
+    ref = C.gemv(L.x, L.theta, L.q[cols], L.s[cols], L.z[cols], spec.b_max)
+    _check_y(y[torch.from_numpy(cols).to(dev)], ref, TOL_F32, "fp32")
+    _check_y(yb[torch.from_numpy(cols).to(dev)], ref, TOL_BF16, "bf16")
+    bits = O.assign_bits(L.x, L.theta, spec.b_max)
+    say(f"  eff bits {O.eff_bits(bits):.3f}")
+    del dl
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("eff", [2, 3, 4, 8])
+def test_full_llama8b_linears(dev, eff):
+    for spec in S.llama8b_linears(eff):
+        _full_linear_check(spec, dev)
+
+
+@pytest.mark.parametrize("eff", [1.5, 2, 3, 4])
+def test_full_llama8b_linears_b4(dev, eff):
+    for spec in S.llama8b_linears_b4(eff):
+        _full_linear_check(spec, dev)
+
+
+@pytest.mark.parametrize("eff", [2, 3])
+def test_full_llama70b_linears(dev, eff):
+    rng = np.random.default_rng(70)
+    for spec in S.llama70b_linears(eff):
+        cols = np.unique(np.concatenate([[0, spec.d_out - 1], rng.integers(0, spec.d_out, 1024)]))
+        _full_linear_check(spec, dev, sample=cols)
+
+
+@pytest.mark.parametrize("eff,n_layers", [(3, 32), (2, 2), (4, 2), (6, 2), (8, 2)])
+def test_full_decode_step_sampled(dev, eff, n_layers):
+    """Every linear of the 32-layer 8B decode step (codes drawn on the device
+    from a seeded generator), 64 sampled outputs of each checked against the
+    oracle on the same code rows."""
+    import torch
+    specs = S.llama8b_decode_step(eff, n_layers)
+    say(f"decode step eff={eff} layers={n_layers} linears={len(specs)}")
+    worst = 0.0
+    for spec in specs:
+        g = torch.Generator(device=dev)
+        g.manual_seed(S.torch_seed(spec.key, 0))
+        q_dev = torch.randint(0, 256, (spec.d_out, spec.d_in), generator=g, dtype=torch.uint8, device=dev)
+        Lin = S.make_linear(spec, with_codes=False)
+        dl = DeviceLinear(None, Lin.s, Lin.z, 8, dev, q_dev=q_dev)
+        y = dl.gemv(to_dev_x(Lin.x, "bf16", dev), _theta_dev(Lin.theta, dev), torch.float32)
+        rng = np.random.default_rng(spec.key[2] * 10 + spec.key[3])
+        cols = np.unique(np.concatenate([[0, spec.d_out - 1], rng.integers(0, spec.d_out, 64)]))
+        cols_t = torch.from_numpy(cols).to(dev)
+        q_rows = q_dev.index_select(0, cols_t).cpu().numpy()
+        ref = C.gemv(Lin.x, Lin.theta, q_rows, Lin.s[cols], Lin.z[cols], 8)
+        err = O.max_rel_error(y[cols_t].cpu().numpy(), ref)
+        worst = max(worst, err)
+        assert err <= TOL_F32, (spec, err)
+        del dl, q_dev
+    say(f"  worst rel err {worst:.3e}")
