@@ -123,12 +123,47 @@ grinqh_status grinqh_assign_bits(const grinqh_layout* L, const void* x, grinqh_d
  *              must be zero-filled before its first use; every call leaves it
  *              ready for the next call (no clearing between calls).  Calls
  *              sharing one workspace must not overlap in time.
- * x and y must not overlap.  Accumulation is fp32 in a fixed order, so
- * repeated calls on the same inputs give bit-identical y. */
+ * The packed planes of L must be smaller than 4 GiB (EINVAL otherwise).
+ * x and y must not overlap.  Accumulation is fp32; the partial sums of the
+ * input-channel slices are combined with fp32 atomic adds, so repeated calls
+ * may differ in the last bits of y (b_i, the loaded planes and the codes are
+ * always identical).  The workspace must be device memory (hipMalloc). */
 grinqh_status grinqh_gemv(const grinqh_layout* L, const void* x, grinqh_dtype x_dtype,
                           const float* theta, const uint32_t* planes, const uint16_t* s,
                           const uint16_t* z, void* y, grinqh_dtype y_dtype, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* Operands of one GEMV in a group call (all device pointers, same meaning and
+ * alignment as the grinqh_gemv arguments of the same names). */
+typedef struct {
+    const void* x;
+    const float* theta;
+    const uint32_t* planes;
+    const uint16_t* s;
+    const uint16_t* z;
+    void* y;
+} grinqh_gemv_operands;
+
+#define GRINQH_MAX_GROUP 8
+
+/* Workspace bytes for grinqh_gemv_group over these layouts (host arrays of n
+ * entries); 0 if an argument is invalid or no device is visible. */
+size_t grinqh_gemv_group_workspace_bytes(const grinqh_layout* layouts, int32_t n);
+
+/* n (1 .. GRINQH_MAX_GROUP) independent decode GEMVs in one kernel launch,
+ * e.g. the q/k/v or gate/up projections of a decoder layer, or any set of
+ * linears whose inputs are ready.  Each member computes exactly what
+ * grinqh_gemv computes for its own x, theta, planes, s, z and y (KD1-KD3);
+ * one launch lets the members' memory latencies overlap.
+ *   layouts    host array [n]; every layout must have the same b_max.
+ *   ops        host array [n] of operands.
+ *   x_dtype, y_dtype  shared by all members.
+ *   workspace  >= grinqh_gemv_group_workspace_bytes(layouts, n) bytes,
+ *              256-byte aligned, zero-filled before first use, self-clearing.
+ * The members' outputs must not overlap each other or any member's input. */
+grinqh_status grinqh_gemv_group(const grinqh_layout* layouts, const grinqh_gemv_operands* ops,
+                                int32_t n, grinqh_dtype x_dtype, grinqh_dtype y_dtype,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Test and diagnostic call: the truncated codes q_b * 2^(b_max - b_i)
  * (KD3's spliced truncated integer, at full scale) that the GEMV kernel's own

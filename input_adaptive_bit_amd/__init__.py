@@ -9,5 +9,6 @@ from .grinqh import (  # noqa: F401
     GRINQH_BF16, GRINQH_F32, GrinqhError, Layout, EXPORTS, load, status_string,
     grinqh_layout_init, grinqh_packed_bytes, grinqh_gemv_workspace_bytes,
     grinqh_pack, grinqh_assign_bits, grinqh_gemv, grinqh_debug_codes,
-    new_workspace, pack, assign_bits, gemv, debug_codes,
+    grinqh_gemv_group_workspace_bytes, grinqh_gemv_group, Operands, MAX_GROUP,
+    new_workspace, new_group_workspace, pack, assign_bits, gemv, debug_codes,
 )

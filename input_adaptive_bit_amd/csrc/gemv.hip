@@ -1,18 +1,38 @@
-// The decode GEMV (GRINQH note, key designs 1-3), first version.
+// The decode GEMV of GRINQH (papernotes.org note, key designs 1-3) for gfx950.
 //
-//   kernel 1 (partial): workgroup = (output tile of 1024, slice of input
-//     channels).  Each wave takes every 4th channel of the slice, assigns its
-//     bit width from |x_i| and the thresholds, and for a loaded channel reads
-//     only the first b_i/2 plane rows of the tile (one uint32 = 16 outputs
-//     per lane), accumulating x_i * 4^(P-1-p) * fragment in fp32.  The four
-//     waves are summed through LDS and the tile's partial sums are stored.
-//     The tile-0 workgroup of each slice also stores S = sum x_i and
-//     C = sum x_i * phi_i over the slice's loaded channels.
-//   kernel 2 (epilogue): y_j = s_j * (A_j + C) + z_j * S with A_j the sum of
-//     the slices' partials, in slice order.
+// One launch computes one or several independent GEMVs (a "group", all with
+// the same b_max).  Work item = (GEMV, output tile of T outputs, slice of
+// `chunk` input channels); one 256-thread workgroup per item.
 //
-// y_j = sum_i x_i * (s_j * (code_ij + phi_i) + z_j) regroups exactly into
-// s_j * (A_j + C) + z_j * S, so the per-output work is one FMA per fragment.
+// Prologue (key design 1).  The workgroup reads its slice of x, assigns
+// b_i = 2 * #{k : theta_k <= |x_i|} with exact fp32 compares and bucket-sorts
+// the loaded channels (b_i > 0) by plane count Pi = b_i / 2 into LDS, in
+// ascending channel order inside each bucket (wave ballots + prefix sums, so
+// the order - and with it the fp32 summation order - is fixed).  It also
+// forms the slice's S = sum x_i and C = sum x_i * phi_i over loaded channels.
+//
+// Main loop (key design 2).  A wave is split into G lane groups of 64/G
+// lanes; lane r of a group owns 16*V consecutive outputs of the tile.  Each
+// group takes one channel of the current bucket at a time and reads only its
+// first Pi plane rows: V words (4*V bytes) per lane per plane, so a group
+// reads T/4 contiguous bytes per plane row and untaken planes and skipped
+// channels issue no memory request.  Because every channel in a bucket has
+// the same plane count, the lanes of a wave never diverge.
+//
+// Decode and accumulate (key design 3).  The Pi plane words of 16 outputs are
+// merged in integer registers into byte codes (decode.hpp), each byte is
+// converted with one v_cvt_f32_ubyte and accumulated with one fp32 FMA into
+// acc_j += x_i * 4^(P-Pi) * code.  With A_j = sum_i x_i * code_ij,
+//   y_j = sum_i x_i * (s_j * (code_ij + phi_i) + z_j) = s_j * (A_j + C) + z_j * S.
+//
+// Reduction.  Lane groups are summed with cross-lane shuffles, waves through
+// LDS; the tile's partial A_j + C_slice is added with fp32 atomics into a
+// workspace row and S_slice into a per-tile slot.  A per-tile arrival counter
+// elects the last workgroup, which applies the epilogue
+// y_j = s_j * acc_j + z_j * S (bf16 output rounded to nearest even) and
+// clears its workspace row and counter for the next call.
+#include <cstdlib>
+
 #include "decode.hpp"
 #include "internal.h"
 
@@ -21,154 +41,411 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kTileOut = kWave * 16;      // 1024 outputs: one word per lane
+constexpr int kMaxChunk = kThreads;       // one channel per thread in the prologue
+constexpr int kV = 2;                     // plane words per lane per plane row (8-byte loads)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-template <int P>
-__global__ __launch_bounds__(kThreads) void gemv_partial_kernel(
-    const void* __restrict__ x, int x_dtype, const float* __restrict__ theta,
-    const uint32_t* __restrict__ planes, int d_in, int row_words, int chunk, int padded_out,
-    float* __restrict__ partials, float* __restrict__ sc) {
-    constexpr int b_max = 2 * P;
-    __shared__ float red[kWaves][kTileOut];
-    __shared__ float sc_red[2][kWaves];
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-    const int tile = blockIdx.x;
-    const int split = blockIdx.y;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
-    float th[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < P; ++k) th[k] = theta[k];
+// Plane rows are read through a raw buffer resource covering the packed
+// planes.  A lane with nothing to load uses an offset past the end: the
+// load returns zeros without a memory request, so every load instruction is
+// unconditional and the wait counters stay exact (no branches around loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t planes_rsrc(const uint32_t* planes, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(planes), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
 
-    const int i0 = split * chunk;
-    const int i1 = min(d_in, i0 + chunk);
-    const int word = tile * kWave + lane;
-    const bool has_word = word < row_words;
+constexpr int kNonTemporal = 2;   // plane rows are streamed once per call
 
-    float acc[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) acc[t] = 0.f;
-
-    for (int i = i0 + wv; i < i1; i += kWaves) {
-        const float xv = load_x(x, x_dtype, i);
-        const int Pi = bits_of<P>(xv, th) >> 1;            // planes to read
-        const uint32_t* row = planes + static_cast<size_t>(i) * P * row_words + word;
-        for (int p = 0; p < Pi; ++p) {
-            const uint32_t wd = has_word ? row[static_cast<size_t>(p) * row_words] : 0u;
-            const float alpha = xv * plane_weight<P>(p);
-#pragma unroll
-            for (int t = 0; t < 16; ++t) acc[t] += alpha * static_cast<float>(fragment(wd, t));
-        }
-    }
-
-#pragma unroll
-    for (int t = 0; t < 16; ++t) red[wv][lane * 16 + t] = acc[t];
-    __syncthreads();
-    for (int o = threadIdx.x; o < kTileOut; o += kThreads) {
-        float v = red[0][o];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) v += red[w][o];
-        partials[static_cast<size_t>(split) * padded_out + tile * kTileOut + o] = v;
-    }
-
-    if (tile == 0) {
-        // S and C over this slice: fixed-order tree, so runs are identical.
-        float S = 0.f, C = 0.f;
-        for (int i = i0 + threadIdx.x; i < i1; i += kThreads) {
-            const float xv = load_x(x, x_dtype, i);
-            const int b = bits_of<P>(xv, th);
-            if (b > 0) {
-                S += xv;
-                C += xv * phi_of(b_max, b);
-            }
-        }
-#pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) {
-            S += __shfl_xor(S, off);
-            C += __shfl_xor(C, off);
-        }
-        if (lane == 0) {
-            sc_red[0][wv] = S;
-            sc_red[1][wv] = C;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            float s_tot = sc_red[0][0], c_tot = sc_red[1][0];
-            for (int w = 1; w < kWaves; ++w) {
-                s_tot += sc_red[0][w];
-                c_tot += sc_red[1][w];
-            }
-            sc[2 * split] = s_tot;
-            sc[2 * split + 1] = c_tot;
-        }
+template <int V>
+__device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_off, uint32_t (&w)[V]) {
+    if constexpr (V == 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_off, 0, kNonTemporal);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, byte_off, 0, kNonTemporal);
+        w[0] = v.x; w[1] = v.y;
     }
 }
 
-__global__ __launch_bounds__(kThreads) void gemv_epilogue_kernel(
-    const float* __restrict__ partials, const float* __restrict__ sc, int n_splits,
-    int padded_out, const uint16_t* __restrict__ s, const uint16_t* __restrict__ z,
-    void* __restrict__ y, int y_dtype, int d_out) {
-    const int j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= d_out) return;
-    float A = 0.f, S = 0.f, C = 0.f;
-    for (int sp = 0; sp < n_splits; ++sp) {
-        A += partials[static_cast<size_t>(sp) * padded_out + j];
-        S += sc[2 * sp];
-        C += sc[2 * sp + 1];
+// acc[16 v + 4 b + k] += x_scaled * unscale(k) * byte b of E_v[k]
+template <int Pb, int V>
+__device__ __forceinline__ void accumulate(float (&acc)[16 * V], const uint32_t (&w)[Pb][V], float xs) {
+    float a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = xs * code_unscale<Pb>(k);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        uint32_t pw[Pb];
+#pragma unroll
+        for (int p = 0; p < Pb; ++p) pw[p] = w[p][v];
+        uint32_t E[4];
+        merge_codes<Pb>(pw, E);
+        // Hide the known-zero bits of E from the optimiser so that each byte
+        // becomes one v_cvt_f32_ubyte{0..3} instead of a bit-field extract
+        // followed by a conversion.
+#pragma unroll
+        for (int k = 0; k < 4; ++k) asm("" : "+v"(E[k]));
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                acc[16 * v + 4 * b + k] = __builtin_fmaf(a[k], byte_f32(E[k], b), acc[16 * v + 4 * b + k]);
     }
-    const float r = f16_to_f32(s[j]) * (A + C) + f16_to_f32(z[j]) * S;
-    if (y_dtype == GRINQH_F32)
-        static_cast<float*>(y)[j] = r;
-    else
-        static_cast<uint16_t*>(y)[j] = f32_to_bf16_rne(r);
+}
+
+struct SliceLists {
+    int idx[kMaxChunk];        // channel index
+    float xv[kMaxChunk];       // x_i (fp32)
+    int start[5];              // bucket Pi starts at start[Pi - 1] .. start[Pi]
+    int wave_cnt[4][kWaves];   // per-level wave counts
+    float red_s[kWaves], red_c[kWaves];
+    int is_last;
+};
+
+// Registers for U channels of one bucket (Pb planes each) of one worker.
+template <int Pb, int V, int U>
+struct Batch {
+    uint32_t w[U][Pb][V];
+    float xs[U];
+    bool ok[U];
+};
+
+// Issues the plane loads of bucket entries e0, e0 + stride, ... (U of them).
+// Entries past the bucket end, and lanes whose words lie past the padded
+// row, load from past the end of the buffer (zeros, no request).
+struct PlaneSrc {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t oob;           // an offset past the end of the planes
+    uint32_t row_bytes;     // bytes per plane row
+    uint32_t lane_bytes;    // byte offset of this lane's words within a row
+};
+
+template <int P, int Pb, int V, int U>
+__device__ __forceinline__ void load_batch(Batch<Pb, V, U>& B, const SliceLists& L, int e0, int stride,
+                                           int end, const PlaneSrc& src, bool lane_ok) {
+    const float pscale = static_cast<float>(1u << (2 * (P - Pb)));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * stride;
+        const bool ok = lane_ok && e < end;
+        const int ec = e < end ? e : 0;
+        const int i = L.idx[ec];
+        B.ok[u] = ok;
+        B.xs[u] = ok ? L.xv[ec] * pscale : 0.f;
+        const uint32_t base = static_cast<uint32_t>(i) * P * src.row_bytes + src.lane_bytes;
+#pragma unroll
+        for (int p = 0; p < Pb; ++p)
+            load_words<V>(src.rsrc, ok ? base + static_cast<uint32_t>(p) * src.row_bytes : src.oob, B.w[u][p]);
+    }
+}
+
+// Decodes the batch slot by slot; a slot that no lane group of the wave has a
+// channel for is skipped as a whole (wave-uniform branch), so small buckets
+// cost only the slots they fill.
+template <int Pb, int V, int U>
+__device__ __forceinline__ void compute_batch(float (&acc)[16 * V], const Batch<Pb, V, U>& B) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (__ballot(B.ok[u]) != 0ull) accumulate<Pb, V>(acc, B.w[u], B.xs[u]);
+}
+
+// Channels in flight per worker and bucket: the first batch of every bucket
+// is issued before any decoding starts, so a workgroup with a typical slice
+// waits for one memory round trip rather than one per bucket.
+template <int Pb>
+struct BatchSize { static constexpr int U = Pb == 4 ? 2 : Pb == 3 ? 2 : 3; };
+
+template <int P, int Pb, int V, int G>
+struct Bucket {
+    static constexpr int U = BatchSize<Pb>::U;
+    static constexpr int stride = kWaves * G;
+    Batch<Pb, V, U> B;
+    int e, end;
+    __device__ __forceinline__ void first(const SliceLists& L, int worker, const PlaneSrc& src, bool lane_ok) {
+        e = L.start[Pb - 1] + worker;
+        end = L.start[Pb];
+        load_batch<P, Pb, V, U>(B, L, e, stride, end, src, lane_ok);
+    }
+    __device__ __forceinline__ void finish(float (&acc)[16 * V], const SliceLists& L, const PlaneSrc& src,
+                                           bool lane_ok) {
+        compute_batch<Pb, V, U>(acc, B);
+        for (e += stride * U; e < end; e += stride * U) {
+            load_batch<P, Pb, V, U>(B, L, e, stride, end, src, lane_ok);
+            compute_batch<Pb, V, U>(acc, B);
+        }
+    }
+};
+
+template <int P, int V, int G>
+__global__ __launch_bounds__(kThreads, 4) void gemv_kernel(GemvGroupArgs args) {
+    constexpr int b_max = 2 * P;
+    constexpr int LG = kWave / G;            // lanes per group
+    constexpr int T = LG * 16 * V;           // outputs per tile
+    constexpr int NW = kWaves * G;           // workers (lane groups) per workgroup
+    __shared__ SliceLists L;
+    __shared__ float red[NW][T];             // one partial row per worker
+
+    // ---- locate the GEMV and the (tile, slice) of this workgroup
+    int d = 0;
+    while (d + 1 < args.n && static_cast<int>(blockIdx.x) >= args.g[d + 1].wg_begin) ++d;
+    const GemvDesc& D = args.g[d];
+    const int local = static_cast<int>(blockIdx.x) - D.wg_begin;
+    const int tile = local % D.n_tiles;
+    const int split = local / D.n_tiles;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wv = tid / kWave;
+
+    float th[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < P; ++k) th[k] = D.theta[k];
+
+    // ---- prologue: bit assignment and bucket sort of the slice (key design 1)
+    const int i0 = split * D.chunk;
+    const int cnt = min(D.chunk, D.d_in - i0);
+    float xv = 0.f;
+    int pi = 0;
+    if (tid < cnt) {
+        xv = load_x(D.x, D.x_dtype, i0 + tid);
+        pi = bits_of<P>(xv, th) >> 1;
+    }
+    int rank[4];
+#pragma unroll
+    for (int l = 0; l < P; ++l) {
+        const unsigned long long m = __ballot(pi == l + 1);
+        rank[l] = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == 0) L.wave_cnt[l][wv] = __popcll(m);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int acc_start = 0;
+        L.start[0] = 0;
+        for (int l = 0; l < P; ++l) {
+            for (int w = 0; w < kWaves; ++w) acc_start += L.wave_cnt[l][w];
+            L.start[l + 1] = acc_start;
+        }
+        for (int l = P; l < 4; ++l) L.start[l + 1] = acc_start;
+    }
+    __syncthreads();
+    if (pi > 0) {
+        int pos = L.start[pi - 1] + rank[pi - 1];
+        for (int w = 0; w < wv; ++w) pos += L.wave_cnt[pi - 1][w];
+        L.idx[pos] = i0 + tid;
+        L.xv[pos] = xv;
+    }
+    __syncthreads();
+
+    // ---- main loop (key designs 2 and 3)
+    const int group = lane / LG;
+    const int r = lane % LG;
+    const int word_off = tile * (T / 16) + r * V;      // first word of this lane in a plane row
+    const bool lane_ok = word_off + V <= D.row_words;
+    const int worker = wv * G + group;
+    float acc[16 * V];
+#pragma unroll
+    for (int o = 0; o < 16 * V; ++o) acc[o] = 0.f;
+    PlaneSrc src;
+    src.row_bytes = static_cast<uint32_t>(D.row_words) * 4u;
+    src.oob = src.row_bytes * static_cast<uint32_t>(P) * static_cast<uint32_t>(D.d_in);
+    src.rsrc = planes_rsrc(D.planes, src.oob);
+    src.lane_bytes = static_cast<uint32_t>(word_off) * 4u;
+    Bucket<P, 1, V, G> k1;
+    Bucket<P, (P >= 2 ? 2 : 1), V, G> k2;
+    Bucket<P, (P >= 3 ? 3 : 1), V, G> k3;
+    Bucket<P, (P >= 4 ? 4 : 1), V, G> k4;
+    if constexpr (P >= 4) k4.first(L, worker, src, lane_ok);
+    if constexpr (P >= 3) k3.first(L, worker, src, lane_ok);
+    if constexpr (P >= 2) k2.first(L, worker, src, lane_ok);
+    k1.first(L, worker, src, lane_ok);
+    if constexpr (P >= 4) k4.finish(acc, L, src, lane_ok);
+    if constexpr (P >= 3) k3.finish(acc, L, src, lane_ok);
+    if constexpr (P >= 2) k2.finish(acc, L, src, lane_ok);
+    k1.finish(acc, L, src, lane_ok);
+
+    // slice sums S and C over loaded channels (fixed-order reduction); they
+    // are only needed by the epilogue, so they stay off the load path
+    {
+        float s_part = pi > 0 ? xv : 0.f;
+        float c_part = pi > 0 ? xv * phi_of(b_max, 2 * pi) : 0.f;
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) {
+            s_part += __shfl_xor(s_part, off);
+            c_part += __shfl_xor(c_part, off);
+        }
+        if (lane == 0) {
+            L.red_s[wv] = s_part;
+            L.red_c[wv] = c_part;
+        }
+    }
+
+    // ---- reduction: every worker stores its partial row to LDS, then each
+    // thread sums the NW copies of its outputs in worker order (fixed order)
+#pragma unroll
+    for (int o = 0; o < 16 * V; o += 4)
+        *reinterpret_cast<float4*>(&red[worker][r * 16 * V + o]) =
+            make_float4(acc[o], acc[o + 1], acc[o + 2], acc[o + 3]);
+    __syncthreads();
+    float s_slice = L.red_s[0], c_slice = L.red_c[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+        s_slice += L.red_s[w];
+        c_slice += L.red_c[w];
+    }
+    float* ws_acc = D.acc + static_cast<size_t>(tile) * T;
+#pragma unroll
+    for (int o = tid; o < T; o += kThreads) {
+        float v = red[0][o];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += red[w][o];
+        unsafeAtomicAdd(ws_acc + o, v + c_slice);
+    }
+    unsigned* ctrl = D.ctrl + static_cast<size_t>(tile) * kCtrlWords;   // own 256-byte line per tile
+    float* ssum = reinterpret_cast<float*>(ctrl + 1);
+    if (tid == 0) unsafeAtomicAdd(ssum, s_slice);
+
+    // ---- last workgroup of the tile applies the epilogue.  No device-scope
+    // fence: fp32 atomics are performed at the device coherence point, so each
+    // thread waits until its own atomics have completed (s_waitcnt 0) before the
+    // arrival count is taken, and the elected workgroup reads the row back with
+    // agent-scope loads.  (A __threadfence here writes back and invalidates the
+    // L2 for every workgroup, which serialises the whole grid.)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(ctrl, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        L.is_last = (prev == static_cast<unsigned>(D.n_splits - 1)) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!L.is_last) return;
+    const float S = __hip_atomic_load(ssum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int j0 = tile * T;
+    for (int o = tid; o < T; o += kThreads) {
+        const int j = j0 + o;
+        const float a = __hip_atomic_load(ws_acc + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ws_acc + o, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (j < D.d_out) {
+            const float yv = f16_to_f32(D.s[j]) * a + f16_to_f32(D.z[j]) * S;
+            if (D.y_dtype == GRINQH_F32)
+                static_cast<float*>(D.y)[j] = yv;
+            else
+                static_cast<uint16_t*>(D.y)[j] = f32_to_bf16_rne(yv);
+        }
+    }
+    if (tid == 0) {
+        __hip_atomic_store(ssum, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ctrl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <int P, int V, int G>
+hipError_t launch_t(const GemvGroupArgs& a, int total_wg, hipStream_t stream) {
+    gemv_kernel<P, V, G><<<dim3(static_cast<unsigned>(total_wg)), dim3(kThreads), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int P>
+hipError_t launch_p(const GemvGroupArgs& a, int G, int total_wg, hipStream_t stream) {
+    switch (G) {
+        case 1: return launch_t<P, kV, 1>(a, total_wg, stream);
+        case 2: return launch_t<P, kV, 2>(a, total_wg, stream);
+        case 4: return launch_t<P, kV, 4>(a, total_wg, stream);
+        case 8: return launch_t<P, kV, 8>(a, total_wg, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev) {
+int gemv_tile_outputs(int G) { return (kWave / G) * 16 * kV; }
+
+// Optional launch-shape overrides for tuning on new shapes:
+// GRINQH_LANE_GROUPS (1, 2, 4 or 8) and GRINQH_CHUNK (1 .. 256 channels).
+int env_int(const char* name) {
+    const char* v = std::getenv(name);
+    return v ? std::atoi(v) : 0;
+}
+
+GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_groups) {
+    const int env_groups = env_int("GRINQH_LANE_GROUPS");
+    const int env_chunk = env_int("GRINQH_CHUNK");
     GemvPlan pl{};
-    pl.tile_outputs = kTileOut;
-    pl.n_tiles = (L.row_words + kWave - 1) / kWave;
-    // Aim for about 4 workgroups per CU, with at least 16 channels per slice.
-    const int want_wg = 4 * dev.cu_count;
-    int n_splits = (want_wg + pl.n_tiles - 1) / pl.n_tiles;
-    const int max_splits = (L.d_in + 15) / 16;
-    if (n_splits > max_splits) n_splits = max_splits;
+    const int padded = L.row_words * 16;
+    // Tile: 4 lane groups of 16 lanes, 512 outputs (128-byte plane-row
+    // segments per group); wide outputs use wider tiles to bound the tile count.
+    int G = 4;
+    if (padded >= 4096 * 7) G = 2;
+    if (env_groups == 1 || env_groups == 2 || env_groups == 4 || env_groups == 8) G = env_groups;
+    if (lane_groups == 1 || lane_groups == 2 || lane_groups == 4 || lane_groups == 8) G = lane_groups;
+    pl.lane_groups = G;
+    pl.tile_outputs = gemv_tile_outputs(G);
+    pl.n_tiles = (padded + pl.tile_outputs - 1) / pl.tile_outputs;
+    // Slices of about 128 input channels: each worker then holds a typical
+    // slice's taken plane rows in one batch of loads.
+    int n_splits = (L.d_in + 127) / 128;
+    if (env_chunk >= 1 && env_chunk <= kMaxChunk) n_splits = (L.d_in + env_chunk - 1) / env_chunk;
+    (void)dev;
+    const int min_splits = (L.d_in + kMaxChunk - 1) / kMaxChunk;
+    if (n_splits < min_splits) n_splits = min_splits;
+    if (n_splits > L.d_in) n_splits = L.d_in;
     if (n_splits < 1) n_splits = 1;
     pl.chunk = (L.d_in + n_splits - 1) / n_splits;
     pl.n_splits = (L.d_in + pl.chunk - 1) / pl.chunk;
-    const size_t padded_out = static_cast<size_t>(pl.n_tiles) * kTileOut;
-    pl.ws_partials = 0;
-    pl.ws_counters = align_up(static_cast<size_t>(pl.n_splits) * padded_out * sizeof(float), 256);
-    pl.ws_bytes = align_up(pl.ws_counters + static_cast<size_t>(pl.n_splits) * 2 * sizeof(float), 256);
+    const size_t acc_bytes = static_cast<size_t>(pl.n_tiles) * pl.tile_outputs * sizeof(float);
+    pl.ws_acc = 0;
+    pl.ws_ctrl = align_up(acc_bytes, 256);
+    pl.ws_bytes = pl.ws_ctrl + static_cast<size_t>(pl.n_tiles) * kCtrlWords * sizeof(unsigned);
     return pl;
+}
+
+void fill_desc(GemvDesc* g, const grinqh_layout& L, const GemvPlan& plan, const void* x, int x_dtype,
+               const float* theta, const uint32_t* planes, const uint16_t* s, const uint16_t* z,
+               void* y, int y_dtype, void* workspace, int wg_begin) {
+    char* ws = static_cast<char*>(workspace);
+    g->x = x;
+    g->theta = theta;
+    g->planes = planes;
+    g->s = s;
+    g->z = z;
+    g->y = y;
+    g->acc = reinterpret_cast<float*>(ws + plan.ws_acc);
+    g->ctrl = reinterpret_cast<unsigned*>(ws + plan.ws_ctrl);
+    g->d_in = L.d_in;
+    g->d_out = L.d_out;
+    g->row_words = L.row_words;
+    g->chunk = plan.chunk;
+    g->n_splits = plan.n_splits;
+    g->n_tiles = plan.n_tiles;
+    g->wg_begin = wg_begin;
+    g->x_dtype = x_dtype;
+    g->y_dtype = y_dtype;
+}
+
+hipError_t launch_gemv_group(int n_planes, int lane_groups, const GemvGroupArgs& args, int total_wg,
+                             hipStream_t stream) {
+    switch (n_planes) {
+        case 1: return launch_p<1>(args, lane_groups, total_wg, stream);
+        case 2: return launch_p<2>(args, lane_groups, total_wg, stream);
+        case 3: return launch_p<3>(args, lane_groups, total_wg, stream);
+        case 4: return launch_p<4>(args, lane_groups, total_wg, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_gemv(const grinqh_layout& L, const GemvPlan& plan, const void* x,
                        int x_dtype, const float* theta, const uint32_t* planes,
                        const uint16_t* s, const uint16_t* z, void* y, int y_dtype,
                        void* workspace, hipStream_t stream) {
-    char* ws = static_cast<char*>(workspace);
-    float* partials = reinterpret_cast<float*>(ws + plan.ws_partials);
-    float* sc = reinterpret_cast<float*>(ws + plan.ws_counters);
-    const int padded_out = plan.n_tiles * kTileOut;
-    dim3 grid(static_cast<unsigned>(plan.n_tiles), static_cast<unsigned>(plan.n_splits));
-    dim3 block(kThreads);
-    switch (L.n_planes) {
-        case 1: gemv_partial_kernel<1><<<grid, block, 0, stream>>>(x, x_dtype, theta, planes, L.d_in, L.row_words, plan.chunk, padded_out, partials, sc); break;
-        case 2: gemv_partial_kernel<2><<<grid, block, 0, stream>>>(x, x_dtype, theta, planes, L.d_in, L.row_words, plan.chunk, padded_out, partials, sc); break;
-        case 3: gemv_partial_kernel<3><<<grid, block, 0, stream>>>(x, x_dtype, theta, planes, L.d_in, L.row_words, plan.chunk, padded_out, partials, sc); break;
-        case 4: gemv_partial_kernel<4><<<grid, block, 0, stream>>>(x, x_dtype, theta, planes, L.d_in, L.row_words, plan.chunk, padded_out, partials, sc); break;
-        default: return hipErrorInvalidValue;
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    dim3 grid2(static_cast<unsigned>((L.d_out + kThreads - 1) / kThreads));
-    gemv_epilogue_kernel<<<grid2, block, 0, stream>>>(partials, sc, plan.n_splits, padded_out, s, z,
-                                                      y, y_dtype, L.d_out);
-    return hipGetLastError();
+    GemvGroupArgs a{};
+    a.n = 1;
+    fill_desc(&a.g[0], L, plan, x, x_dtype, theta, planes, s, z, y, y_dtype, workspace, 0);
+    return launch_gemv_group(L.n_planes, plan.lane_groups, a, plan.n_tiles * plan.n_splits, stream);
 }
 
 }  // namespace grinqh

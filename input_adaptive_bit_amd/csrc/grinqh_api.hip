@@ -26,9 +26,37 @@ bool valid_layout(const grinqh_layout* L) {
 
 bool valid_dtype(int d) { return d == GRINQH_BF16 || d == GRINQH_F32; }
 
+// The GEMV kernel addresses the planes with 32-bit byte offsets.
+constexpr size_t kMaxGemvPlaneBytes = 0xFFFFFF00u;
+
+size_t packed_bytes(const grinqh_layout* L) {
+    return static_cast<size_t>(L->d_in) * L->n_planes * L->row_words * 4u;
+}
+
 int dtype_bytes(int d) { return d == GRINQH_BF16 ? 2 : 4; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// The common tile width of a group: the narrowest any member would pick.
+int group_lane_groups(const grinqh_layout* layouts, int n, const DeviceInfo& dev) {
+    int G = 1;
+    for (int k = 0; k < n; ++k) {
+        const int g = plan_gemv(layouts[k], dev).lane_groups;
+        if (g > G) G = g;
+    }
+    return G;
+}
+
+size_t group_ws_bytes(const grinqh_layout* layouts, int n, const DeviceInfo& dev, int G) {
+    size_t total = 0;
+    for (int k = 0; k < n; ++k) total += plan_gemv(layouts[k], dev, G).ws_bytes;
+    return total;
+}
 
 grinqh_status map_error(hipError_t e) {
     if (e == hipSuccess) return GRINQH_OK;
@@ -145,6 +173,7 @@ grinqh_status grinqh_gemv(const grinqh_layout* L, const void* x, grinqh_dtype x_
         s == nullptr || z == nullptr || y == nullptr || workspace == nullptr)
         return GRINQH_EINVAL;
     if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return GRINQH_EINVAL;
+    if (packed_bytes(L) > kMaxGemvPlaneBytes) return GRINQH_EINVAL;
     if (!aligned(x, dtype_bytes(x_dtype)) || !aligned(y, dtype_bytes(y_dtype)) ||
         !aligned(theta, 4) || !aligned(planes, 16) || !aligned(s, 2) || !aligned(z, 2) ||
         !aligned(workspace, 256))
@@ -164,6 +193,61 @@ grinqh_status grinqh_gemv(const grinqh_layout* L, const void* x, grinqh_dtype x_
     if (workspace_bytes < plan.ws_bytes) return GRINQH_ENOSPACE;
     return map_error(launch_gemv(*L, plan, x, x_dtype, theta, planes, s, z, y, y_dtype,
                                  workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t grinqh_gemv_group_workspace_bytes(const grinqh_layout* layouts, int32_t n) {
+    if (layouts == nullptr || n < 1 || n > GRINQH_MAX_GROUP) return 0;
+    for (int k = 0; k < n; ++k)
+        if (!valid_layout(&layouts[k]) || layouts[k].b_max != layouts[0].b_max) return 0;
+    DeviceInfo dev;
+    hipError_t e;
+    if (!current_device_info(&dev, &e)) return 0;
+    return group_ws_bytes(layouts, n, dev, group_lane_groups(layouts, n, dev));
+}
+
+grinqh_status grinqh_gemv_group(const grinqh_layout* layouts, const grinqh_gemv_operands* ops,
+                                int32_t n, grinqh_dtype x_dtype, grinqh_dtype y_dtype,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (layouts == nullptr || ops == nullptr || workspace == nullptr) return GRINQH_EINVAL;
+    if (n < 1 || n > GRINQH_MAX_GROUP) return GRINQH_EINVAL;
+    if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return GRINQH_EINVAL;
+    if (!aligned(workspace, 256)) return GRINQH_EALIGN;
+    const size_t xb = dtype_bytes(x_dtype), yb = dtype_bytes(y_dtype);
+    for (int k = 0; k < n; ++k) {
+        const grinqh_layout* L = &layouts[k];
+        const grinqh_gemv_operands& o = ops[k];
+        if (!valid_layout(L) || L->b_max != layouts[0].b_max) return GRINQH_EINVAL;
+        if (packed_bytes(L) > kMaxGemvPlaneBytes) return GRINQH_EINVAL;
+        if (!o.x || !o.theta || !o.planes || !o.s || !o.z || !o.y) return GRINQH_EINVAL;
+        if (!aligned(o.x, xb) || !aligned(o.y, yb) || !aligned(o.theta, 4) || !aligned(o.planes, 16) ||
+            !aligned(o.s, 2) || !aligned(o.z, 2))
+            return GRINQH_EALIGN;
+    }
+    for (int k = 0; k < n; ++k) {
+        const size_t ny = static_cast<size_t>(layouts[k].d_out) * yb;
+        for (int m = 0; m < n; ++m) {
+            if (overlap(ops[k].y, ny, ops[m].x, static_cast<size_t>(layouts[m].d_in) * xb)) return GRINQH_EINVAL;
+            if (m != k && overlap(ops[k].y, ny, ops[m].y, static_cast<size_t>(layouts[m].d_out) * yb))
+                return GRINQH_EINVAL;
+        }
+    }
+    DeviceInfo dev;
+    hipError_t e;
+    if (!current_device_info(&dev, &e)) return map_error(e);
+    const int G = group_lane_groups(layouts, n, dev);
+    if (workspace_bytes < group_ws_bytes(layouts, n, dev, G)) return GRINQH_ENOSPACE;
+    GemvGroupArgs args{};
+    args.n = n;
+    char* ws = static_cast<char*>(workspace);
+    int wg = 0;
+    for (int k = 0; k < n; ++k) {
+        const GemvPlan plan = plan_gemv(layouts[k], dev, G);
+        fill_desc(&args.g[k], layouts[k], plan, ops[k].x, x_dtype, ops[k].theta, ops[k].planes, ops[k].s,
+                  ops[k].z, ops[k].y, y_dtype, ws, wg);
+        ws += plan.ws_bytes;
+        wg += plan.n_tiles * plan.n_splits;
+    }
+    return map_error(launch_gemv_group(layouts[0].n_planes, G, args, wg, static_cast<hipStream_t>(stream)));
 }
 
 grinqh_status grinqh_debug_codes(const grinqh_layout* L, const uint8_t* bits,

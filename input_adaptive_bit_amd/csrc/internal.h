@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/grinqh.h"
+#include "grinqh.h"
 
 namespace grinqh {
 
@@ -26,16 +26,47 @@ hipError_t launch_assign_bits(const grinqh_layout& L, const void* x, int x_dtype
 
 // Launch plan of the GEMV for a layout on a device (pure host arithmetic).
 struct GemvPlan {
-    int tile_outputs;   // outputs per workgroup tile
+    int lane_groups;    // lane groups per wave (1, 2, 4 or 8)
+    int tile_outputs;   // outputs per workgroup tile: (64 / lane_groups) * 64
     int n_tiles;        // ceil(padded d_out / tile_outputs)
-    int chunk;          // input channels per split
+    int chunk;          // input channels per slice (<= 256)
     int n_splits;       // ceil(d_in / chunk)
-    size_t ws_partials; // byte offset of the fp32 partial sums
-    size_t ws_counters; // byte offset of the per-tile arrival counters
+    size_t ws_acc;      // byte offset of the fp32 accumulators [n_tiles * tile_outputs]
+    size_t ws_ctrl;     // byte offset of the per-tile control blocks (256 bytes each:
+                        // arrival counter, then the sum of x over loaded channels)
     size_t ws_bytes;    // total workspace bytes
 };
 
-GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev);
+// One GEMV of a launch group (kernel argument, passed by value).
+struct GemvDesc {
+    const void* x;
+    const float* theta;
+    const uint32_t* planes;
+    const uint16_t* s;
+    const uint16_t* z;
+    void* y;
+    float* acc;
+    unsigned* ctrl;
+    int d_in, d_out, row_words, chunk, n_splits, n_tiles, wg_begin, x_dtype, y_dtype;
+};
+
+constexpr int kMaxGroup = 8;
+constexpr int kCtrlWords = 64;       // one 256-byte line per tile
+
+struct GemvGroupArgs {
+    GemvDesc g[kMaxGroup];
+    int n;
+};
+
+// lane_groups = 0: the plan picks the tile width; otherwise it is forced.
+GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_groups = 0);
+
+void fill_desc(GemvDesc* g, const grinqh_layout& L, const GemvPlan& plan, const void* x, int x_dtype,
+               const float* theta, const uint32_t* planes, const uint16_t* s, const uint16_t* z,
+               void* y, int y_dtype, void* workspace, int wg_begin);
+
+hipError_t launch_gemv_group(int n_planes, int lane_groups, const GemvGroupArgs& args, int total_wg,
+                             hipStream_t stream);
 
 hipError_t launch_gemv(const grinqh_layout& L, const GemvPlan& plan, const void* x,
                        int x_dtype, const float* theta, const uint32_t* planes,

@@ -36,9 +36,16 @@ class Layout(ctypes.Structure):
                 f"n_planes={self.n_planes}, row_words={self.row_words})")
 
 
+class Operands(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("theta", ctypes.c_void_p), ("planes", ctypes.c_void_p),
+                ("s", ctypes.c_void_p), ("z", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+MAX_GROUP = 8
+
 EXPORTS = ("grinqh_version", "grinqh_status_string", "grinqh_layout_init", "grinqh_packed_bytes",
            "grinqh_gemv_workspace_bytes", "grinqh_pack", "grinqh_assign_bits", "grinqh_gemv",
-           "grinqh_debug_codes")
+           "grinqh_gemv_group_workspace_bytes", "grinqh_gemv_group", "grinqh_debug_codes")
 
 _lib = None
 
@@ -77,6 +84,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.grinqh_assign_bits.restype = ctypes.c_int
     lib.grinqh_gemv.argtypes = [LP, vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
     lib.grinqh_gemv.restype = ctypes.c_int
+    OP = ctypes.POINTER(Operands)
+    lib.grinqh_gemv_group_workspace_bytes.argtypes = [LP, i32]
+    lib.grinqh_gemv_group_workspace_bytes.restype = sz
+    lib.grinqh_gemv_group.argtypes = [LP, OP, i32, ctypes.c_int, ctypes.c_int, vp, sz, vp]
+    lib.grinqh_gemv_group.restype = ctypes.c_int
     lib.grinqh_debug_codes.argtypes = [LP, vp, vp, vp, vp]
     lib.grinqh_debug_codes.restype = ctypes.c_int
     if path is None:
@@ -185,6 +197,36 @@ def grinqh_gemv(L: Layout, x, theta, planes, s, z, y, workspace, stream=None) ->
            "grinqh_gemv")
 
 
+def grinqh_gemv_group_workspace_bytes(layouts) -> int:
+    arr = (Layout * len(layouts))(*layouts)
+    return int(load().grinqh_gemv_group_workspace_bytes(arr, len(layouts)))
+
+
+def grinqh_gemv_group(layouts, operands, workspace, stream=None) -> None:
+    """operands: one (x, theta, planes, s, z, y) tuple of tensors per layout."""
+    import torch
+    n = len(layouts)
+    if n != len(operands):
+        raise ValueError("one operand tuple per layout")
+    ops = (Operands * n)()
+    for k, (L, (x, theta, planes, s, z, y)) in enumerate(zip(layouts, operands)):
+        _need(x, "x", (torch.bfloat16, torch.float32), L.d_in * x.element_size())
+        _need(theta, "theta", (torch.float32,), 4 * L.n_planes)
+        _need(planes, "planes", (torch.int32, torch.uint32), grinqh_packed_bytes(L))
+        _need(s, "s", (torch.float16,), 2 * L.d_out)
+        _need(z, "z", (torch.float16,), 2 * L.d_out)
+        _need(y, "y", (torch.bfloat16, torch.float32), L.d_out * y.element_size())
+        if _dtype_code(x) != _dtype_code(operands[0][0]) or _dtype_code(y) != _dtype_code(operands[0][5]):
+            raise TypeError("every member of a group shares the x and y dtypes")
+        ops[k] = Operands(_ptr(x), _ptr(theta), _ptr(planes), _ptr(s), _ptr(z), _ptr(y))
+    _need(workspace, "workspace", None)
+    arr = (Layout * n)(*layouts)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().grinqh_gemv_group(arr, ops, n, _dtype_code(operands[0][0]), _dtype_code(operands[0][5]),
+                                    _ptr(workspace), ws_bytes, _stream(stream)),
+           "grinqh_gemv_group")
+
+
 def grinqh_debug_codes(L: Layout, bits, planes, codes, stream=None) -> None:
     import torch
     _need(bits, "bits", (torch.uint8,), L.d_in)
@@ -203,6 +245,15 @@ def new_workspace(L: Layout, device=None):
     n = grinqh_gemv_workspace_bytes(L)
     if n == 0:
         raise GrinqhError(GRINQH_ENODEV, "grinqh_gemv_workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def new_group_workspace(layouts, device=None):
+    """A zero-filled workspace tensor for grinqh_gemv_group over `layouts`."""
+    import torch
+    n = grinqh_gemv_group_workspace_bytes(layouts)
+    if n == 0:
+        raise GrinqhError(GRINQH_EINVAL, "grinqh_gemv_group_workspace_bytes")
     return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
 
 

@@ -126,3 +126,33 @@ def test_argument_checks_before_any_device_call():
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         B.load(str(tmp_path / "missing.so"))
+
+
+def test_group_argument_checks_before_any_device_call():
+    lib = G.load()
+    A = 1 << 16
+    Ls = [G.grinqh_layout_init(256, 128, 8), G.grinqh_layout_init(128, 64, 8)]
+    arr = (B.Layout * 2)(*Ls)
+    ops = (B.Operands * 2)(B.Operands(A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A),
+                           B.Operands(7 * A, 8 * A, 9 * A, 10 * A, 11 * A, 12 * A))
+    WS = 13 * A
+    call = lambda n=2, a=arr, o=ops, xd=0, yd=0, ws=WS: lib.grinqh_gemv_group(a, o, n, xd, yd, ws, 1 << 30, None)
+    assert call(n=0) == B.GRINQH_EINVAL
+    assert call(n=9) == B.GRINQH_EINVAL
+    assert call(a=None) == B.GRINQH_EINVAL
+    assert call(o=None) == B.GRINQH_EINVAL
+    assert call(xd=3) == B.GRINQH_EINVAL
+    assert call(ws=None) == B.GRINQH_EINVAL
+    assert call(ws=WS + 8) == B.GRINQH_EALIGN
+    bad = (B.Layout * 2)(Ls[0], G.grinqh_layout_init(128, 64, 4))           # mixed b_max
+    assert call(a=bad) == B.GRINQH_EINVAL
+    o2 = (B.Operands * 2)(ops[0], B.Operands(7 * A, 8 * A, 9 * A + 4, 10 * A, 11 * A, 12 * A))
+    assert call(o=o2) == B.GRINQH_EALIGN                                     # planes misaligned
+    o3 = (B.Operands * 2)(ops[0], B.Operands(7 * A, 8 * A, 9 * A, 10 * A, 11 * A, 6 * A + 64))
+    assert call(o=o3) == B.GRINQH_EINVAL                                     # outputs overlap
+    o4 = (B.Operands * 2)(ops[0], B.Operands(7 * A, 8 * A, 9 * A, 10 * A, 11 * A, A + 16))
+    assert call(o=o4) == B.GRINQH_EINVAL                                     # output overlaps an input
+    o5 = (B.Operands * 2)(ops[0], B.Operands(None, 8 * A, 9 * A, 10 * A, 11 * A, 12 * A))
+    assert call(o=o5) == B.GRINQH_EINVAL
+    assert lib.grinqh_gemv_group_workspace_bytes(bad, 2) == 0
+    assert lib.grinqh_gemv_group_workspace_bytes(arr, 0) == 0

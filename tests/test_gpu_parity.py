@@ -47,15 +47,24 @@ def _run_and_check(dl, x_f32, x_dtype, theta, y_ref, what, dev, check_bf16=True)
     y32 = dl.gemv(xd, td, torch.float32)
     y32b = dl.gemv(xd, td, torch.float32)
     torch.cuda.synchronize()
-    assert torch.equal(y32.view(torch.int32), y32b.view(torch.int32)), f"{what}: not deterministic"
     y = _check_y(y32, y_ref, TOL_F32, what + " fp32")
+    # a second call (workspace reused, slices combined in another order) agrees
+    # to fp32 rounding
+    y2 = y32b.cpu().numpy().astype(np.float64)
+    assert O.max_rel_error(y2, y) <= 5e-4, f"{what}: repeated call differs"
     if check_bf16:
         yb = dl.gemv(xd, td, torch.bfloat16)
         torch.cuda.synchronize()
         _check_y(yb, y_ref, TOL_BF16, what + " bf16")
+        # bf16 output is the fp32 result rounded to nearest even; the fp32 values
+        # of two calls may differ in the last bits, so allow one bf16 step
         rne = O.round_to_bf16(y.astype(np.float32))
         got = yb.view(torch.int16).cpu().numpy().view(np.uint16)
-        assert np.array_equal(got, rne), f"{what}: bf16 output is not RNE of the fp32 output"
+        gotf = yb.float().cpu().numpy().astype(np.float64)
+        floor = 1e-2 * float(np.sqrt(np.mean(y ** 2))) if y.size else 0.0
+        assert np.all(np.abs(gotf - y) <= 2.0 ** -8 * np.maximum(np.abs(y), floor) + 1e-30), \
+            f"{what}: bf16 output is not the rounded fp32 output"
+        assert np.mean(got == rne) >= 0.99, f"{what}: bf16 output is not RNE of the fp32 output"
     return y
 
 
@@ -269,7 +278,8 @@ def test_gemv_power_of_two_scaling_is_exact(dev):
         ym = dl.gemv(to_dev_x(np.ldexp(x, m).astype(np.float32), "bf16", dev),
                      _theta_dev(np.ldexp(theta, m).astype(np.float32), dev), torch.float32)
         torch.cuda.synchronize()
-        assert torch.equal(ym, y0 * (2.0 ** m))
+        # same bits, same codes; y scales by 2^m up to the order of the slice sums
+        assert O.max_rel_error((ym / (2.0 ** m)).cpu().numpy(), y0.cpu().numpy()) <= 5e-4
 
 
 # ------------------------------------------------- full-size workloads ------
@@ -339,3 +349,103 @@ def test_full_decode_step_sampled(dev, eff, n_layers):
         assert err <= TOL_F32, (spec, err)
         del dl, q_dev
     say(f"  worst rel err {worst:.3e}")
+
+
+def test_gemv_graph_replays_match_eager(dev):
+    """The GEMV captured in a HIP graph: every replay, with eager work and
+    synchronisations in between, matches the eager call (the kernels use no
+    memset; the workspace clears itself)."""
+    import torch
+    rng = np.random.default_rng(10)
+    d_in, d_out = 4096, 4096
+    q = rng.integers(0, 256, size=(d_out, d_in), dtype=np.uint8)
+    s = rng.uniform(0.001, 0.01, d_out).astype(np.float16)
+    z = rng.normal(0, 0.01, d_out).astype(np.float16)
+    x = S.bf16_bits_to_f32(S.f32_to_bf16_bits(rng.standard_t(3, d_in).astype(np.float32)))
+    theta = np.sort(np.quantile(np.abs(x), [0.2, 0.52, 0.82, 0.96])).astype(np.float32)
+    dl = DeviceLinear(q, s, z, 8, dev)
+    xd = to_dev_x(x, "bf16", dev)
+    td = _theta_dev(theta, dev)
+    say("gemv graph replays")
+    eager = dl.gemv(xd, td, torch.float32).clone()
+    y_ref = C.gemv(x, theta, q, s, z, 8)
+    import input_adaptive_bit_amd as G
+    y = torch.empty(d_out, dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        G.grinqh_gemv(dl.L, xd, td, dl.planes, dl.s, dl.z, y, dl.ws)
+    for rep in range(5):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        assert O.max_rel_error(got, eager.cpu().numpy()) <= 5e-4, rep
+        assert O.max_rel_error(got, y_ref) <= TOL_F32, rep
+        _ = dl.gemv(xd, td, torch.float32)      # eager work between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("d_in,d_out", [(4096, 14336), (14336, 4096), (4096, 4096)])
+def test_gemv_exact_integer_sums_many_calls(dev, d_in, d_out):
+    """Small-integer activations, s = 1, z = 1: every partial sum is a multiple
+    of 1/2 below 2^23, so fp32 accumulation is exact in any order and y must
+    equal the oracle exactly on every one of 20 back-to-back calls (a lost or
+    stale cross-workgroup update would show as a mismatch)."""
+    import torch
+    rng = np.random.default_rng(d_in + d_out)
+    q = rng.integers(0, 256, size=(d_out, d_in), dtype=np.uint8)
+    s = np.ones(d_out, np.float16)
+    z = np.ones(d_out, np.float16)
+    theta = np.array([1.0, 2.0, 3.0, 4.0], np.float32)
+    dl = DeviceLinear(q, s, z, 8, dev)
+    td = _theta_dev(theta, dev)
+    say(f"exact integer sums {d_in}->{d_out}")
+    xs = [rng.choice(np.array([0.5, 1, 2, 3, 4, -1, -2, -3, -4, -0.5], np.float32), d_in) for _ in range(20)]
+    outs = [dl.gemv(to_dev_x(x, "bf16", dev), td, torch.float32) for x in xs]
+    torch.cuda.synchronize()
+    for n, (x, y) in enumerate(zip(xs, outs)):
+        ref = C.gemv(x, theta, q, s, z, 8)
+        assert np.max(np.abs(ref)) < 2 ** 23
+        got = y.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref), (n, int(np.sum(got != ref)))
+
+
+@pytest.mark.parametrize("b_max,x_dtype", [(8, "bf16"), (4, "bf16"), (8, "f32")])
+def test_gemv_group_matches_oracle_and_single_calls(dev, b_max, x_dtype):
+    """A group launch of differently shaped members: each member matches the
+    oracle and the single-GEMV call on the same inputs."""
+    import torch
+    import input_adaptive_bit_amd as G
+    shapes = [(4096, 4096), (4096, 1024), (4096, 14336), (14336, 4096), (300, 1500), (1, 65)]
+    rng = np.random.default_rng(77 + b_max)
+    members, ops, refs, singles = [], [], [], []
+    say(f"group launch b_max={b_max} x={x_dtype} members={len(shapes)}")
+    for di, do in shapes:
+        q = rng.integers(0, 1 << b_max, size=(do, di), dtype=np.uint8)
+        s = rng.uniform(0.001, 0.01, do).astype(np.float16)
+        z = rng.normal(0, 0.01, do).astype(np.float16)
+        x = rng.standard_t(3, di).astype(np.float32)
+        if x_dtype == "bf16":
+            x = S.bf16_bits_to_f32(S.f32_to_bf16_bits(x))
+        theta = np.sort(np.quantile(np.abs(x), np.linspace(0.2, 0.9, b_max // 2))).astype(np.float32)
+        dl = DeviceLinear(q, s, z, b_max, dev)
+        xd, td = to_dev_x(x, x_dtype, dev), _theta_dev(theta, dev)
+        y = torch.empty(do, dtype=torch.float32, device=dev)
+        members.append(dl)
+        ops.append((xd, td, dl.planes, dl.s, dl.z, y))
+        refs.append(C.gemv(x, theta, q, s, z, b_max))
+        singles.append(dl.gemv(xd, td, torch.float32))
+    layouts = [m.L for m in members]
+    ws = G.new_group_workspace(layouts, dev)
+    for rep in range(3):
+        for o in ops:
+            o[5].fill_(float("nan"))
+        G.grinqh_gemv_group(layouts, ops, ws)
+        torch.cuda.synchronize()
+        for k, (o, ref, single) in enumerate(zip(ops, refs, singles)):
+            got = o[5].cpu().numpy()
+            err = O.max_rel_error(got, ref)
+            assert err <= TOL_F32, (rep, k, err)
+            assert O.max_rel_error(got, single.cpu().numpy()) <= 5e-4, (rep, k)
