@@ -2,7 +2,9 @@
 //
 // One launch computes one or several independent GEMVs (a "group", all with
 // the same b_max).  Work item = (GEMV, output tile of T outputs, slice of
-// `chunk` input channels); one 256-thread workgroup per item.
+// `chunk` input channels); one 256-thread workgroup per item.  The slice
+// length is chosen from the whole launch so that all items are resident at
+// once (about four workgroups per CU): one generation of workgroups.
 //
 // Prologue (key design 1).  The workgroup reads its slice of x, assigns
 // b_i = 2 * #{k : theta_k <= |x_i|} with exact fp32 compares and bucket-sorts
@@ -12,12 +14,15 @@
 // forms the slice's S = sum x_i and C = sum x_i * phi_i over loaded channels.
 //
 // Main loop (key design 2).  A wave is split into G lane groups of 64/G
-// lanes; lane r of a group owns 16*V consecutive outputs of the tile.  Each
-// group takes one channel of the current bucket at a time and reads only its
-// first Pi plane rows: V words (4*V bytes) per lane per plane, so a group
-// reads T/4 contiguous bytes per plane row and untaken planes and skipped
-// channels issue no memory request.  Because every channel in a bucket has
-// the same plane count, the lanes of a wave never diverge.
+// lanes; lane r of a group owns 16*V consecutive outputs of the tile.  The
+// 4G groups of the workgroup ("workers") take the channels of a bucket in
+// turn and read only their first Pi plane rows: V words (4*V bytes) per lane
+// per plane, so a group reads T/4 contiguous bytes per plane row, and
+// untaken planes and skipped channels issue no memory request.  Every
+// channel in a bucket has the same plane count, so the lanes of a wave never
+// diverge.  The first batch of every bucket - sized to hold a typical
+// slice's share - is issued before any decoding, so a workgroup waits for
+// about one memory round trip.
 //
 // Decode and accumulate (key design 3).  The Pi plane words of 16 outputs are
 // merged in integer registers into byte codes (decode.hpp), each byte is
@@ -42,6 +47,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxChunk = kThreads;       // one channel per thread in the prologue
+constexpr int kMinChunk = 64;
+constexpr int kWgPerCu = 4;               // resident workgroups per CU the kernel is sized for
 constexpr int kV = 2;                     // plane words per lane per plane row (8-byte loads)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -106,17 +113,18 @@ struct SliceLists {
     int is_last;
 };
 
-// Registers for U channels of one bucket (Pb planes each) of one worker.
+// Plane words of U channels of one bucket (Pb planes each) of one worker.
+// x_i stays in LDS until the decode, so a batch holds only plane words.
 template <int Pb, int V, int U>
 struct Batch {
     uint32_t w[U][Pb][V];
-    float xs[U];
-    bool ok[U];
 };
 
-// Issues the plane loads of bucket entries e0, e0 + stride, ... (U of them).
-// Entries past the bucket end, and lanes whose words lie past the padded
-// row, load from past the end of the buffer (zeros, no request).
+// Issues the plane loads of bucket entries e0, e0 + stride, ... (U of
+// them).  Entries past the bucket end load from past the end of the buffer
+// (zeros, no request).  Lanes whose words lie past the padded row read
+// whatever follows in the buffer: they only feed padded outputs, which are
+// never written and which the epilogue clears.
 struct PlaneSrc {
     __amdgpu_buffer_rsrc_t rsrc;
     uint32_t oob;           // an offset past the end of the planes
@@ -126,17 +134,12 @@ struct PlaneSrc {
 
 template <int P, int Pb, int V, int U>
 __device__ __forceinline__ void load_batch(Batch<Pb, V, U>& B, const SliceLists& L, int e0, int stride,
-                                           int end, const PlaneSrc& src, bool lane_ok) {
-    const float pscale = static_cast<float>(1u << (2 * (P - Pb)));
+                                           int end, const PlaneSrc& src) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int e = e0 + u * stride;
-        const bool ok = lane_ok && e < end;
-        const int ec = e < end ? e : 0;
-        const int i = L.idx[ec];
-        B.ok[u] = ok;
-        B.xs[u] = ok ? L.xv[ec] * pscale : 0.f;
-        const uint32_t base = static_cast<uint32_t>(i) * P * src.row_bytes + src.lane_bytes;
+        const bool ok = e < end;
+        const uint32_t base = static_cast<uint32_t>(L.idx[ok ? e : 0]) * (P * src.row_bytes) + src.lane_bytes;
 #pragma unroll
         for (int p = 0; p < Pb; ++p)
             load_words<V>(src.rsrc, ok ? base + static_cast<uint32_t>(p) * src.row_bytes : src.oob, B.w[u][p]);
@@ -146,18 +149,25 @@ __device__ __forceinline__ void load_batch(Batch<Pb, V, U>& B, const SliceLists&
 // Decodes the batch slot by slot; a slot that no lane group of the wave has a
 // channel for is skipped as a whole (wave-uniform branch), so small buckets
 // cost only the slots they fill.
-template <int Pb, int V, int U>
-__device__ __forceinline__ void compute_batch(float (&acc)[16 * V], const Batch<Pb, V, U>& B) {
+template <int P, int Pb, int V, int U>
+__device__ __forceinline__ void compute_batch(float (&acc)[16 * V], const Batch<Pb, V, U>& B,
+                                              const SliceLists& L, int e0, int stride, int end) {
+    const float pscale = static_cast<float>(1u << (2 * (P - Pb)));
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-        if (__ballot(B.ok[u]) != 0ull) accumulate<Pb, V>(acc, B.w[u], B.xs[u]);
+    for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * stride;
+        const bool ok = e < end;
+        if (__ballot(ok) == 0ull) continue;
+        const float xs = ok ? L.xv[e] * pscale : 0.f;
+        accumulate<Pb, V>(acc, B.w[u], xs);
+    }
 }
 
 // Channels in flight per worker and bucket: the first batch of every bucket
-// is issued before any decoding starts, so a workgroup with a typical slice
-// waits for one memory round trip rather than one per bucket.
+// is issued before any decoding starts, and a batch holds a typical slice's
+// share of its bucket, so a workgroup waits for about one memory round trip.
 template <int Pb>
-struct BatchSize { static constexpr int U = Pb == 4 ? 2 : Pb == 3 ? 2 : 3; };
+struct BatchSize { static constexpr int U = Pb == 4 ? 1 : Pb == 3 ? 3 : Pb == 2 ? 5 : 6; };
 
 template <int P, int Pb, int V, int G>
 struct Bucket {
@@ -165,23 +175,22 @@ struct Bucket {
     static constexpr int stride = kWaves * G;
     Batch<Pb, V, U> B;
     int e, end;
-    __device__ __forceinline__ void first(const SliceLists& L, int worker, const PlaneSrc& src, bool lane_ok) {
+    __device__ __forceinline__ void first(const SliceLists& L, int worker, const PlaneSrc& src) {
         e = L.start[Pb - 1] + worker;
         end = L.start[Pb];
-        load_batch<P, Pb, V, U>(B, L, e, stride, end, src, lane_ok);
+        load_batch<P, Pb, V, U>(B, L, e, stride, end, src);
     }
-    __device__ __forceinline__ void finish(float (&acc)[16 * V], const SliceLists& L, const PlaneSrc& src,
-                                           bool lane_ok) {
-        compute_batch<Pb, V, U>(acc, B);
+    __device__ __forceinline__ void finish(float (&acc)[16 * V], const SliceLists& L, const PlaneSrc& src) {
+        compute_batch<P, Pb, V, U>(acc, B, L, e, stride, end);
         for (e += stride * U; e < end; e += stride * U) {
-            load_batch<P, Pb, V, U>(B, L, e, stride, end, src, lane_ok);
-            compute_batch<Pb, V, U>(acc, B);
+            load_batch<P, Pb, V, U>(B, L, e, stride, end, src);
+            compute_batch<P, Pb, V, U>(acc, B, L, e, stride, end);
         }
     }
 };
 
 template <int P, int V, int G>
-__global__ __launch_bounds__(kThreads, 4) void gemv_kernel(GemvGroupArgs args) {
+__global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs args) {
     constexpr int b_max = 2 * P;
     constexpr int LG = kWave / G;            // lanes per group
     constexpr int T = LG * 16 * V;           // outputs per tile
@@ -243,7 +252,6 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(GemvGroupArgs args) {
     const int group = lane / LG;
     const int r = lane % LG;
     const int word_off = tile * (T / 16) + r * V;      // first word of this lane in a plane row
-    const bool lane_ok = word_off + V <= D.row_words;
     const int worker = wv * G + group;
     float acc[16 * V];
 #pragma unroll
@@ -257,14 +265,14 @@ __global__ __launch_bounds__(kThreads, 4) void gemv_kernel(GemvGroupArgs args) {
     Bucket<P, (P >= 2 ? 2 : 1), V, G> k2;
     Bucket<P, (P >= 3 ? 3 : 1), V, G> k3;
     Bucket<P, (P >= 4 ? 4 : 1), V, G> k4;
-    if constexpr (P >= 4) k4.first(L, worker, src, lane_ok);
-    if constexpr (P >= 3) k3.first(L, worker, src, lane_ok);
-    if constexpr (P >= 2) k2.first(L, worker, src, lane_ok);
-    k1.first(L, worker, src, lane_ok);
-    if constexpr (P >= 4) k4.finish(acc, L, src, lane_ok);
-    if constexpr (P >= 3) k3.finish(acc, L, src, lane_ok);
-    if constexpr (P >= 2) k2.finish(acc, L, src, lane_ok);
-    k1.finish(acc, L, src, lane_ok);
+    if constexpr (P >= 4) k4.first(L, worker, src);
+    if constexpr (P >= 3) k3.first(L, worker, src);
+    if constexpr (P >= 2) k2.first(L, worker, src);
+    k1.first(L, worker, src);
+    if constexpr (P >= 4) k4.finish(acc, L, src);
+    if constexpr (P >= 3) k3.finish(acc, L, src);
+    if constexpr (P >= 2) k2.finish(acc, L, src);
+    k1.finish(acc, L, src);
 
     // slice sums S and C over loaded channels (fixed-order reduction); they
     // are only needed by the epilogue, so they stay off the load path
@@ -372,7 +380,7 @@ int env_int(const char* name) {
     return v ? std::atoi(v) : 0;
 }
 
-GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_groups) {
+GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_groups, double launch_area) {
     const int env_groups = env_int("GRINQH_LANE_GROUPS");
     const int env_chunk = env_int("GRINQH_CHUNK");
     GemvPlan pl{};
@@ -386,22 +394,32 @@ GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_group
     pl.lane_groups = G;
     pl.tile_outputs = gemv_tile_outputs(G);
     pl.n_tiles = (padded + pl.tile_outputs - 1) / pl.tile_outputs;
-    // Slices of about 128 input channels: each worker then holds a typical
-    // slice's taken plane rows in one batch of loads.
-    int n_splits = (L.d_in + 127) / 128;
-    if (env_chunk >= 1 && env_chunk <= kMaxChunk) n_splits = (L.d_in + env_chunk - 1) / env_chunk;
-    (void)dev;
-    const int min_splits = (L.d_in + kMaxChunk - 1) / kMaxChunk;
-    if (n_splits < min_splits) n_splits = min_splits;
-    if (n_splits > L.d_in) n_splits = L.d_in;
+    // Slice length: one workgroup per (tile, slice), and about kWgPerCu
+    // workgroups per CU over the whole launch (all members of a group get
+    // the same slice length, so the work per workgroup is even).  That is a
+    // single generation of workgroups: each pays the prologue and the
+    // reduction tail once, and its loads overlap those of all the others.
+    const double area = launch_area > 0 ? launch_area : static_cast<double>(L.d_in) * padded;
+    const double target = static_cast<double>(kWgPerCu) * (dev.cu_count > 0 ? dev.cu_count : 256);
+    int chunk = static_cast<int>(area / (target * pl.tile_outputs) + 0.5);
+    if (chunk < kMinChunk) chunk = kMinChunk;
+    if (chunk > kMaxChunk) chunk = kMaxChunk;
+    if (env_chunk >= 1 && env_chunk <= kMaxChunk) chunk = env_chunk;
+    int n_splits = (L.d_in + chunk - 1) / chunk;
     if (n_splits < 1) n_splits = 1;
-    pl.chunk = (L.d_in + n_splits - 1) / n_splits;
+    pl.chunk = (L.d_in + n_splits - 1) / n_splits;       // balanced slices
     pl.n_splits = (L.d_in + pl.chunk - 1) / pl.chunk;
     const size_t acc_bytes = static_cast<size_t>(pl.n_tiles) * pl.tile_outputs * sizeof(float);
     pl.ws_acc = 0;
     pl.ws_ctrl = align_up(acc_bytes, 256);
     pl.ws_bytes = pl.ws_ctrl + static_cast<size_t>(pl.n_tiles) * kCtrlWords * sizeof(unsigned);
     return pl;
+}
+
+double launch_area(const grinqh_layout& L, int lane_groups) {
+    const int T = gemv_tile_outputs(lane_groups);
+    const int padded = L.row_words * 16;
+    return static_cast<double>(L.d_in) * static_cast<double>((padded + T - 1) / T) * T;
 }
 
 void fill_desc(GemvDesc* g, const grinqh_layout& L, const GemvPlan& plan, const void* x, int x_dtype,

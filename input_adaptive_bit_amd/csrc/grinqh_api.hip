@@ -240,8 +240,10 @@ grinqh_status grinqh_gemv_group(const grinqh_layout* layouts, const grinqh_gemv_
     args.n = n;
     char* ws = static_cast<char*>(workspace);
     int wg = 0;
+    double area = 0;
+    for (int k = 0; k < n; ++k) area += launch_area(layouts[k], G);
     for (int k = 0; k < n; ++k) {
-        const GemvPlan plan = plan_gemv(layouts[k], dev, G);
+        const GemvPlan plan = plan_gemv(layouts[k], dev, G, area);
         fill_desc(&args.g[k], layouts[k], plan, ops[k].x, x_dtype, ops[k].theta, ops[k].planes, ops[k].s,
                   ops[k].z, ops[k].y, y_dtype, ws, wg);
         ws += plan.ws_bytes;

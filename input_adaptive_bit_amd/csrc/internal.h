@@ -59,7 +59,12 @@ struct GemvGroupArgs {
 };
 
 // lane_groups = 0: the plan picks the tile width; otherwise it is forced.
-GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_groups = 0);
+// launch_area: padded d_in x d_out summed over every GEMV of the launch (a
+// group); 0 for a launch of this GEMV alone.  It sets the slice length.
+GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_groups = 0,
+                   double launch_area = 0);
+// Padded d_in x d_out of one GEMV at a tile width, for launch_area.
+double launch_area(const grinqh_layout& L, int lane_groups);
 
 void fill_desc(GemvDesc* g, const grinqh_layout& L, const GemvPlan& plan, const void* x, int x_dtype,
                const float* theta, const uint32_t* planes, const uint16_t* s, const uint16_t* z,
