@@ -1,18 +1,24 @@
 // Test and diagnostic kernel: the truncated codes q_b * 2^(b_max-b) for every
-// loaded channel (GRINQH note, key designs 2-3), decoded by the same SWAR
-// merge the GEMV kernel uses (decode.hpp); skipped channels get 0.
+// loaded channel (GRINQH note, key designs 2-3), decoded by the same routine
+// the GEMV kernel uses (decode_values in decode.hpp); skipped channels get 0.
 #include "decode.hpp"
 #include "internal.h"
 
 namespace grinqh {
 namespace {
 
+// Codes of one word position as the GEMV kernel decodes them: the channel's
+// Pb taken planes go through decode_values<Pb>; value * unit (exact) is the
+// Pb-plane code, times 4^(P-Pb) at full width.
 template <int P, int Pb>
 __device__ __forceinline__ void decode16(const uint32_t* words, uint8_t (&out)[16]) {
-    uint32_t E[4];
-    merge_codes<Pb>(words, E);
+    float val[16];
+    decode_values<Pb>(words, val);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) out[t] = static_cast<uint8_t>(code_from_merged<P, Pb>(E, t));
+    for (int t = 0; t < 16; ++t) {
+        const uint32_t c = static_cast<uint32_t>(val[t] * decode_unit<Pb>(t & 3));
+        out[t] = static_cast<uint8_t>(c << (2 * (P - Pb)));
+    }
 }
 
 template <int P>

@@ -78,29 +78,22 @@ __device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t rsrc, uint32_t
     }
 }
 
-// acc[16 v + 4 b + k] += x_scaled * unscale(k) * byte b of E_v[k]
+// acc[16 v + t] += x_scaled * code(t) for the 16 outputs t of each of the V
+// word positions, code(t) = value(t) * decode_unit(t & 3) (decode.hpp).
 template <int Pb, int V>
 __device__ __forceinline__ void accumulate(float (&acc)[16 * V], const uint32_t (&w)[Pb][V], float xs) {
     float a[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) a[k] = xs * code_unscale<Pb>(k);
+    for (int k = 0; k < 4; ++k) a[k] = xs * decode_unit<Pb>(k);
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         uint32_t pw[Pb];
 #pragma unroll
         for (int p = 0; p < Pb; ++p) pw[p] = w[p][v];
-        uint32_t E[4];
-        merge_codes<Pb>(pw, E);
-        // Hide the known-zero bits of E from the optimiser so that each byte
-        // becomes one v_cvt_f32_ubyte{0..3} instead of a bit-field extract
-        // followed by a conversion.
+        float val[16];
+        decode_values<Pb>(pw, val);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) asm("" : "+v"(E[k]));
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                acc[16 * v + 4 * b + k] = __builtin_fmaf(a[k], byte_f32(E[k], b), acc[16 * v + 4 * b + k]);
+        for (int t = 0; t < 16; ++t) acc[16 * v + t] = __builtin_fmaf(a[t & 3], val[t], acc[16 * v + t]);
     }
 }
 
