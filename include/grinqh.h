@@ -123,7 +123,7 @@ grinqh_status grinqh_assign_bits(const grinqh_layout* L, const void* x, grinqh_d
  *              must be zero-filled before its first use; every call leaves it
  *              ready for the next call (no clearing between calls).  Calls
  *              sharing one workspace must not overlap in time.
- * The packed planes of L must be smaller than 4 GiB (EINVAL otherwise).
+ * The packed planes of L must be smaller than 2 GiB (EINVAL otherwise).
  * x and y must not overlap.  Accumulation is fp32; the partial sums of the
  * input-channel slices are combined with fp32 atomic adds, so repeated calls
  * may differ in the last bits of y (b_i, the loaded planes and the codes are

@@ -67,13 +67,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t planes_rsrc(const uint32_t* pl
 
 constexpr int kNonTemporal = 2;   // plane rows are streamed once per call
 
+// V words at byte offset voff + soff (soff: a wave-uniform plane offset).
 template <int V>
-__device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_off, uint32_t (&w)[V]) {
+__device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                           uint32_t (&w)[V]) {
     if constexpr (V == 4) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_off, 0, kNonTemporal);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, kNonTemporal);
         w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     } else {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, byte_off, 0, kNonTemporal);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, soff, kNonTemporal);
         w[0] = v.x; w[1] = v.y;
     }
 }
@@ -98,8 +100,8 @@ __device__ __forceinline__ void accumulate(float (&acc)[16 * V], const uint32_t 
 }
 
 struct SliceLists {
-    int idx[kMaxChunk];        // channel index
-    float xv[kMaxChunk];       // x_i (fp32)
+    uint32_t off[kMaxChunk];   // byte offset of the channel's plane 0 row: i * P * row_bytes
+    float xv[kMaxChunk];       // x_i * 4^(P - Pi): the multiplier of its Pi-plane code
     int start[5];              // bucket Pi starts at start[Pi - 1] .. start[Pi]
     int wave_cnt[4][kWaves];   // per-level wave counts
     float red_s[kWaves], red_c[kWaves];
@@ -120,10 +122,13 @@ struct Batch {
 // never written and which the epilogue clears.
 struct PlaneSrc {
     __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t oob;           // an offset past the end of the planes
     uint32_t row_bytes;     // bytes per plane row
     uint32_t lane_bytes;    // byte offset of this lane's words within a row
 };
+
+// Base offset of an entry past the bucket end: the planes are smaller than
+// 2 GiB, so this offset plus any plane offset is past the end of the buffer.
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
 template <int P, int Pb, int V, int U>
 __device__ __forceinline__ void load_batch(Batch<Pb, V, U>& B, const SliceLists& L, int e0, int stride,
@@ -132,10 +137,10 @@ __device__ __forceinline__ void load_batch(Batch<Pb, V, U>& B, const SliceLists&
     for (int u = 0; u < U; ++u) {
         const int e = e0 + u * stride;
         const bool ok = e < end;
-        const uint32_t base = static_cast<uint32_t>(L.idx[ok ? e : 0]) * (P * src.row_bytes) + src.lane_bytes;
+        const uint32_t base = (ok ? L.off[e] : kOutOfRange) + src.lane_bytes;
 #pragma unroll
         for (int p = 0; p < Pb; ++p)
-            load_words<V>(src.rsrc, ok ? base + static_cast<uint32_t>(p) * src.row_bytes : src.oob, B.w[u][p]);
+            load_words<V>(src.rsrc, base, static_cast<uint32_t>(p) * src.row_bytes, B.w[u][p]);
     }
 }
 
@@ -145,14 +150,13 @@ __device__ __forceinline__ void load_batch(Batch<Pb, V, U>& B, const SliceLists&
 template <int P, int Pb, int V, int U>
 __device__ __forceinline__ void compute_batch(float (&acc)[16 * V], const Batch<Pb, V, U>& B,
                                               const SliceLists& L, int e0, int stride, int end) {
-    const float pscale = static_cast<float>(1u << (2 * (P - Pb)));
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int e = e0 + u * stride;
         const bool ok = e < end;
         if (__ballot(ok) == 0ull) continue;
-        const float xs = ok ? L.xv[e] * pscale : 0.f;
-        accumulate<Pb, V>(acc, B.w[u], xs);
+        const float xe = L.xv[ok ? e : 0];      // in range either way: no branch
+        accumulate<Pb, V>(acc, B.w[u], ok ? xe : 0.f);
     }
 }
 
@@ -236,8 +240,8 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     if (pi > 0) {
         int pos = L.start[pi - 1] + rank[pi - 1];
         for (int w = 0; w < wv; ++w) pos += L.wave_cnt[pi - 1][w];
-        L.idx[pos] = i0 + tid;
-        L.xv[pos] = xv;
+        L.off[pos] = static_cast<uint32_t>(i0 + tid) * (P * static_cast<uint32_t>(D.row_words) * 4u);
+        L.xv[pos] = xv * static_cast<float>(1u << (2 * (P - pi)));
     }
     __syncthreads();
 
@@ -250,9 +254,9 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
 #pragma unroll
     for (int o = 0; o < 16 * V; ++o) acc[o] = 0.f;
     PlaneSrc src;
-    src.row_bytes = static_cast<uint32_t>(D.row_words) * 4u;
-    src.oob = src.row_bytes * static_cast<uint32_t>(P) * static_cast<uint32_t>(D.d_in);
-    src.rsrc = planes_rsrc(D.planes, src.oob);
+    // the row size is uniform; make that explicit so plane offsets stay scalar
+    src.row_bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(D.row_words) * 4u);
+    src.rsrc = planes_rsrc(D.planes, src.row_bytes * static_cast<uint32_t>(P) * static_cast<uint32_t>(D.d_in));
     src.lane_bytes = static_cast<uint32_t>(word_off) * 4u;
     Bucket<P, 1, V, G> k1;
     Bucket<P, (P >= 2 ? 2 : 1), V, G> k2;
@@ -262,13 +266,9 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     if constexpr (P >= 3) k3.first(L, worker, src);
     if constexpr (P >= 2) k2.first(L, worker, src);
     k1.first(L, worker, src);
-    if constexpr (P >= 4) k4.finish(acc, L, src);
-    if constexpr (P >= 3) k3.finish(acc, L, src);
-    if constexpr (P >= 2) k2.finish(acc, L, src);
-    k1.finish(acc, L, src);
 
-    // slice sums S and C over loaded channels (fixed-order reduction); they
-    // are only needed by the epilogue, so they stay off the load path
+    // slice sums S and C over loaded channels (fixed-order reduction), while
+    // the first plane loads are in flight
     {
         float s_part = pi > 0 ? xv : 0.f;
         float c_part = pi > 0 ? xv * phi_of(b_max, 2 * pi) : 0.f;
@@ -282,6 +282,11 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
             L.red_c[wv] = c_part;
         }
     }
+    if constexpr (P >= 4) k4.finish(acc, L, src);
+    if constexpr (P >= 3) k3.finish(acc, L, src);
+    if constexpr (P >= 2) k2.finish(acc, L, src);
+    k1.finish(acc, L, src);
+
 
     // ---- reduction: every worker stores its partial row to LDS, then each
     // thread sums the NW copies of its outputs in worker order (fixed order)
@@ -297,12 +302,29 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
         c_slice += L.red_c[w];
     }
     float* ws_acc = D.acc + static_cast<size_t>(tile) * T;
+    constexpr int OPT = T / kThreads;                   // outputs per thread
+    // this thread's s_j and z_j, fetched now so that the epilogue, if this
+    // workgroup runs it, does not wait for them
+    float s_j[OPT], z_j[OPT];
 #pragma unroll
-    for (int o = tid; o < T; o += kThreads) {
-        float v = red[0][o];
+    for (int k = 0; k < OPT; ++k) {
+        const int j = tile * T + tid + k * kThreads;
+        const int jc = j < D.d_out ? j : D.d_out - 1;
+        s_j[k] = f16_to_f32(D.s[jc]);
+        z_j[k] = f16_to_f32(D.z[jc]);
+    }
 #pragma unroll
-        for (int w = 1; w < NW; ++w) v += red[w][o];
-        unsafeAtomicAdd(ws_acc + o, v + c_slice);
+    for (int k = 0; k < OPT; ++k) {
+        const int o = tid + k * kThreads;
+        // all NW partials first, then a fixed-order pairwise sum
+        float v[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v[w] = red[w][o];
+#pragma unroll
+        for (int h = NW / 2; h > 0; h /= 2)
+#pragma unroll
+            for (int w = 0; w < h; ++w) v[w] += v[w + h];
+        unsafeAtomicAdd(ws_acc + o, v[0] + c_slice);
     }
     unsigned* ctrl = D.ctrl + static_cast<size_t>(tile) * kCtrlWords;   // own 256-byte line per tile
     float* ssum = reinterpret_cast<float*>(ctrl + 1);
@@ -327,12 +349,14 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     if (!L.is_last) return;
     const float S = __hip_atomic_load(ssum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int j0 = tile * T;
-    for (int o = tid; o < T; o += kThreads) {
+#pragma unroll
+    for (int k = 0; k < OPT; ++k) {
+        const int o = tid + k * kThreads;
         const int j = j0 + o;
         const float a = __hip_atomic_load(ws_acc + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(ws_acc + o, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (j < D.d_out) {
-            const float yv = f16_to_f32(D.s[j]) * a + f16_to_f32(D.z[j]) * S;
+            const float yv = s_j[k] * a + z_j[k] * S;
             if (D.y_dtype == GRINQH_F32)
                 static_cast<float*>(D.y)[j] = yv;
             else

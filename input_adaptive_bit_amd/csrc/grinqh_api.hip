@@ -26,8 +26,10 @@ bool valid_layout(const grinqh_layout* L) {
 
 bool valid_dtype(int d) { return d == GRINQH_BF16 || d == GRINQH_F32; }
 
-// The GEMV kernel addresses the planes with 32-bit byte offsets.
-constexpr size_t kMaxGemvPlaneBytes = 0xFFFFFF00u;
+// The GEMV kernel addresses the planes with 32-bit byte offsets and marks
+// entries past a list end with offsets from 2^31 up, so the planes of one
+// GEMV must stay below 2 GiB.
+constexpr size_t kMaxGemvPlaneBytes = 0x7FFFFF00u;
 
 size_t packed_bytes(const grinqh_layout* L) {
     return static_cast<size_t>(L->d_in) * L->n_planes * L->row_words * 4u;
