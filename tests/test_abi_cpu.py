@@ -107,6 +107,10 @@ def test_argument_checks_before_any_device_call():
     assert gemv(ok(th=TH + 2)) == B.GRINQH_EALIGN
     assert gemv(ok(y=X + 128)) == B.GRINQH_EINVAL          # y overlaps x
     assert lib.grinqh_gemv(None, X, 0, TH, PL, S, Z, Y, 1, WS, 1 << 30, None) == B.GRINQH_EINVAL
+    # the planes of one GEMV must stay below 2 GiB: 2^19 channels x 4 planes x 1 KiB rows is 2 GiB
+    big = G.grinqh_layout_init(1 << 19, 4096, 8)
+    assert G.grinqh_packed_bytes(big) == 1 << 31
+    assert lib.grinqh_gemv(ctypes.byref(big), X, 0, TH, PL, S, Z, Y, 1, WS, 1 << 40, None) == B.GRINQH_EINVAL
 
     assert lib.grinqh_pack(Lp, None, PL, None) == B.GRINQH_EINVAL
     assert lib.grinqh_pack(Lp, X, None, None) == B.GRINQH_EINVAL
