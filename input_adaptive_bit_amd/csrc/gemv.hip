@@ -262,10 +262,17 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     Bucket<P, (P >= 2 ? 2 : 1), V, G> k2;
     Bucket<P, (P >= 3 ? 3 : 1), V, G> k3;
     Bucket<P, (P >= 4 ? 4 : 1), V, G> k4;
+    // Two buckets in flight at a time: the next bucket's first batch is
+    // issued after the bucket two ahead is decoded.  Every workgroup on a CU
+    // then keeps a part of its loads in the CU's queue instead of all of
+    // them, so the resident workgroups are served side by side rather than
+    // one after another.
     if constexpr (P >= 4) k4.first(L, worker, src);
     if constexpr (P >= 3) k3.first(L, worker, src);
-    if constexpr (P >= 2) k2.first(L, worker, src);
-    k1.first(L, worker, src);
+    if constexpr (P <= 2) {
+        if constexpr (P >= 2) k2.first(L, worker, src);
+        k1.first(L, worker, src);
+    }
 
     // slice sums S and C over loaded channels (fixed-order reduction), while
     // the first plane loads are in flight
@@ -283,7 +290,11 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
         }
     }
     if constexpr (P >= 4) k4.finish(acc, L, src);
-    if constexpr (P >= 3) k3.finish(acc, L, src);
+    if constexpr (P >= 3) {
+        k2.first(L, worker, src);
+        k3.finish(acc, L, src);
+        k1.first(L, worker, src);
+    }
     if constexpr (P >= 2) k2.finish(acc, L, src);
     k1.finish(acc, L, src);
 
