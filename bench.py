@@ -13,8 +13,10 @@ bracketed by device synchronisation and HIP events on the launch stream.
 Reported value: required bytes per second, where required bytes = taken
 2-bit planes (sum_i b_i * d_out / 8) + fp16 s and z (4 * d_out), summed over
 the step's GEMVs.  Also reported: the effective-bits sweep 2/3/4/8 (8 = all
-channels at b_max, the dense dequant GEMV of the same kernel), and the plain
-fp64 C oracle timed on the host cores over a bounded sample.
+channels at b_max, the dense dequant GEMV of the same kernel), the whole 32-layer decode step
+(224 GEMVs: per layer one group launch over q, k, v, o, gate, up, down; 7.0 GB
+of planes at b_max 8) at the same effective bits, and the plain fp64 C oracle
+timed on the host cores over a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -136,6 +138,50 @@ class Step:
         G.grinqh_gemv_group(self.layouts, [sh.operands(copy, eff) for sh in self.shapes], self.ws)
 
 
+class DecodeStep:
+    """The whole 32-layer 8B-shaped decode step: per layer one grinqh_gemv_group
+    launch over its 7 linears (q, k, v, o, gate, up, down), each linear with
+    its own activations and thresholds; codes drawn on the device from seeded
+    generators (7.0 GB of planes at b_max 8)."""
+
+    def __init__(self, dev, effs, n_layers=32):
+        import torch
+        import input_adaptive_bit_amd as G
+        import synthetic as S
+        specs = S.llama8b_decode_step(3, n_layers)
+        self.layers = []
+        self.req = {e: 0.0 for e in effs}
+        for layer in range(n_layers):
+            lin_ops = []
+            for spec in specs[layer * 7:(layer + 1) * 7]:
+                g = torch.Generator(device=dev)
+                g.manual_seed(S.torch_seed(spec.key, 0))
+                q = torch.randint(0, 256, (spec.d_out, spec.d_in), generator=g, dtype=torch.uint8, device=dev)
+                L, planes = G.pack(q, 8)
+                del q
+                xs, _ = S.gen_x_stream(spec)
+                s_np, z_np = S.gen_scales(spec)
+                x = torch.from_numpy(S.f32_to_bf16_bits(xs[spec.n_calib]).view(np.int16).copy()).to(dev)
+                th = {}
+                for e in effs:
+                    t = S.calibrate_theta(xs[:spec.n_calib], S.QUANTILES_B8[e], 4)
+                    th[e] = torch.from_numpy(t).to(dev)
+                    bits, _, _ = G.assign_bits(L, x.view(torch.bfloat16), th[e])
+                    self.req[e] += required_bytes(bits.cpu().numpy(), spec.d_out)
+                lin_ops.append(dict(L=L, planes=planes, x=x.view(torch.bfloat16), th=th,
+                                    s=torch.from_numpy(s_np).to(dev), z=torch.from_numpy(z_np).to(dev),
+                                    y=torch.empty(spec.d_out, dtype=torch.bfloat16, device=dev)))
+            layouts = [o["L"] for o in lin_ops]
+            self.layers.append((layouts, lin_ops, G.new_group_workspace(layouts, dev)))
+        torch.cuda.synchronize()
+
+    def launch(self, eff) -> None:
+        import input_adaptive_bit_amd as G
+        for layouts, ops, ws in self.layers:
+            G.grinqh_gemv_group(layouts, [(o["x"], o["th"][eff], o["planes"], o["s"], o["z"], o["y"])
+                                          for o in ops], ws)
+
+
 def capture(fn):
     import torch
     g = torch.cuda.CUDAGraph()
@@ -188,6 +234,8 @@ def main() -> int:
     ap.add_argument("--eff", type=int, default=3, choices=[2, 3, 4, 8])
     ap.add_argument("--sweep-reps", type=int, default=64, help="launches per (eff, shape) sweep point")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-decode-step", action="store_true",
+                    help="skip the 32-layer decode-step measurement (7.0 GB of planes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copies", type=int, default=0, help="weight copies (0: enough for 512 MB)")
@@ -287,6 +335,29 @@ def main() -> int:
             sweep[str(e) if e != 8 else "8 (dense)"] = row
             log(f"sweep eff {e}: " + ", ".join(f"{k} {v['us']} us {v['GB/s']} GB/s" for k, v in row.items()))
 
+    decode_step = {}
+    if not args.no_decode_step:
+        del step
+        for sh in shapes:
+            sh.planes = []
+        torch.cuda.empty_cache()
+        ds = DecodeStep(dev, list(effs))
+        for e in effs:
+            def run_ds(e=e, reps=8):
+                for _ in range(reps):
+                    ds.launch(e)
+            g = capture(run_ds)
+            time_graph(g)
+            t = time_graph(g) * 1e3 / 8
+            gbs = ds.req[e] / (t * 1e-6) / 1e9
+            decode_step[str(e) if e != 8 else "8 (dense)"] = {
+                "us": round(t, 2), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "required_GB": round(ds.req[e] / 1e9, 4), "launches": len(ds.layers)}
+            del g
+            log(f"decode step eff {e}: {t:.1f} us, {gbs:.1f} GB/s")
+        del ds
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(shapes, eff, args.cpu_seconds)
@@ -328,6 +399,7 @@ def main() -> int:
         },
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "decode_step_32_layers": decode_step,
     }
     print(json.dumps(out), flush=True)
     return 0
