@@ -219,29 +219,36 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
         xv = load_x(D.x, D.x_dtype, i0 + tid);
         pi = bits_of<P>(xv, th) >> 1;
     }
-    int rank[4];
+    int rank = 0;
 #pragma unroll
     for (int l = 0; l < P; ++l) {
         const unsigned long long m = __ballot(pi == l + 1);
-        rank[l] = __popcll(m & ((1ull << lane) - 1ull));
+        if (pi == l + 1) rank = __popcll(m & ((1ull << lane) - 1ull));
         if (lane == 0) L.wave_cnt[l][wv] = __popcll(m);
     }
     __syncthreads();
-    if (tid == 0) {
-        int acc_start = 0;
-        L.start[0] = 0;
+    {
+        // every thread forms the bucket starts from the wave counts itself:
+        // bucket Pi = 1 first, each in wave then lane order
+        int pos = rank, acc_start = 0;
+#pragma unroll
         for (int l = 0; l < P; ++l) {
-            for (int w = 0; w < kWaves; ++w) acc_start += L.wave_cnt[l][w];
-            L.start[l + 1] = acc_start;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const int c = L.wave_cnt[l][w];
+                if (l < pi - 1 || (l == pi - 1 && w < wv)) pos += c;
+                acc_start += c;
+            }
+            if (tid == 0) L.start[l + 1] = acc_start;
         }
-        for (int l = P; l < 4; ++l) L.start[l + 1] = acc_start;
-    }
-    __syncthreads();
-    if (pi > 0) {
-        int pos = L.start[pi - 1] + rank[pi - 1];
-        for (int w = 0; w < wv; ++w) pos += L.wave_cnt[pi - 1][w];
-        L.off[pos] = static_cast<uint32_t>(i0 + tid) * (P * static_cast<uint32_t>(D.row_words) * 4u);
-        L.xv[pos] = xv * static_cast<float>(1u << (2 * (P - pi)));
+        if (tid == 0) {
+            L.start[0] = 0;
+            for (int l = P; l < 4; ++l) L.start[l + 1] = acc_start;
+        }
+        if (pi > 0) {
+            L.off[pos] = static_cast<uint32_t>(i0 + tid) * (P * static_cast<uint32_t>(D.row_words) * 4u);
+            L.xv[pos] = xv * static_cast<float>(1u << (2 * (P - pi)));
+        }
     }
     __syncthreads();
 
