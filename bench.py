@@ -13,10 +13,11 @@ bracketed by device synchronisation and HIP events on the launch stream.
 Reported value: required bytes per second, where required bytes = taken
 2-bit planes (sum_i b_i * d_out / 8) + fp16 s and z (4 * d_out), summed over
 the step's GEMVs.  Also reported: the effective-bits sweep 2/3/4/8 (8 = all
-channels at b_max, the dense dequant GEMV of the same kernel), the whole 32-layer decode step
-(224 GEMVs: per layer one group launch over q, k, v, o, gate, up, down; 7.0 GB
-of planes at b_max 8) at the same effective bits, and the plain fp64 C oracle
-timed on the host cores over a bounded sample.
+channels at b_max, the dense dequant GEMV of the same kernel), the whole
+32-layer decode step (128 launches in dependency order: per layer the fused
+q|k|v, o, fused gate|up and down projections; 7.0 GB of planes at b_max 8) at
+the same effective bits, and the plain fp64 C oracle timed on the host cores
+over a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -139,47 +140,45 @@ class Step:
 
 
 class DecodeStep:
-    """The whole 32-layer 8B-shaped decode step: per layer one grinqh_gemv_group
-    launch over its 7 linears (q, k, v, o, gate, up, down), each linear with
-    its own activations and thresholds; codes drawn on the device from seeded
-    generators (7.0 GB of planes at b_max 8)."""
+    """The whole 32-layer 8B-shaped decode step as decode must launch it: per
+    layer the fused q|k|v projection (4096->6144), o (4096->4096), the fused
+    gate|up projection (4096->28672) and down (14336->4096), one grinqh_gemv
+    launch each, in that order (o and down depend on the launch before them),
+    each with its own activations and thresholds; codes drawn on the device
+    from seeded generators (7.0 GB of planes at b_max 8)."""
 
     def __init__(self, dev, effs, n_layers=32):
         import torch
         import input_adaptive_bit_amd as G
         import synthetic as S
         specs = S.llama8b_decode_step(3, n_layers)
-        self.layers = []
+        self.ops = []
         self.req = {e: 0.0 for e in effs}
-        for layer in range(n_layers):
-            lin_ops = []
-            for spec in specs[layer * 7:(layer + 1) * 7]:
-                g = torch.Generator(device=dev)
-                g.manual_seed(S.torch_seed(spec.key, 0))
-                q = torch.randint(0, 256, (spec.d_out, spec.d_in), generator=g, dtype=torch.uint8, device=dev)
-                L, planes = G.pack(q, 8)
-                del q
-                xs, _ = S.gen_x_stream(spec)
-                s_np, z_np = S.gen_scales(spec)
-                x = torch.from_numpy(S.f32_to_bf16_bits(xs[spec.n_calib]).view(np.int16).copy()).to(dev)
-                th = {}
-                for e in effs:
-                    t = S.calibrate_theta(xs[:spec.n_calib], S.QUANTILES_B8[e], 4)
-                    th[e] = torch.from_numpy(t).to(dev)
-                    bits, _, _ = G.assign_bits(L, x.view(torch.bfloat16), th[e])
-                    self.req[e] += required_bytes(bits.cpu().numpy(), spec.d_out)
-                lin_ops.append(dict(L=L, planes=planes, x=x.view(torch.bfloat16), th=th,
-                                    s=torch.from_numpy(s_np).to(dev), z=torch.from_numpy(z_np).to(dev),
-                                    y=torch.empty(spec.d_out, dtype=torch.bfloat16, device=dev)))
-            layouts = [o["L"] for o in lin_ops]
-            self.layers.append((layouts, lin_ops, G.new_group_workspace(layouts, dev)))
+        for spec in specs:
+            g = torch.Generator(device=dev)
+            g.manual_seed(S.torch_seed(spec.key, 0))
+            q = torch.randint(0, 256, (spec.d_out, spec.d_in), generator=g, dtype=torch.uint8, device=dev)
+            L, planes = G.pack(q, 8)
+            del q
+            xs, _ = S.gen_x_stream(spec)
+            s_np, z_np = S.gen_scales(spec)
+            x = torch.from_numpy(S.f32_to_bf16_bits(xs[spec.n_calib]).view(np.int16).copy()).to(dev)
+            th = {}
+            for e in effs:
+                t = S.calibrate_theta(xs[:spec.n_calib], S.QUANTILES_B8[e], 4)
+                th[e] = torch.from_numpy(t).to(dev)
+                bits, _, _ = G.assign_bits(L, x.view(torch.bfloat16), th[e])
+                self.req[e] += required_bytes(bits.cpu().numpy(), spec.d_out)
+            self.ops.append(dict(L=L, planes=planes, x=x.view(torch.bfloat16), th=th,
+                                 s=torch.from_numpy(s_np).to(dev), z=torch.from_numpy(z_np).to(dev),
+                                 y=torch.empty(spec.d_out, dtype=torch.bfloat16, device=dev),
+                                 ws=G.new_workspace(L, dev)))
         torch.cuda.synchronize()
 
     def launch(self, eff) -> None:
         import input_adaptive_bit_amd as G
-        for layouts, ops, ws in self.layers:
-            G.grinqh_gemv_group(layouts, [(o["x"], o["th"][eff], o["planes"], o["s"], o["z"], o["y"])
-                                          for o in ops], ws)
+        for o in self.ops:
+            G.grinqh_gemv(o["L"], o["x"], o["th"][eff], o["planes"], o["s"], o["z"], o["y"], o["ws"])
 
 
 def capture(fn):
@@ -352,7 +351,7 @@ def main() -> int:
             gbs = ds.req[e] / (t * 1e-6) / 1e9
             decode_step[str(e) if e != 8 else "8 (dense)"] = {
                 "us": round(t, 2), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-                "required_GB": round(ds.req[e] / 1e9, 4), "launches": len(ds.layers)}
+                "required_GB": round(ds.req[e] / 1e9, 4), "launches": len(ds.ops)}
             del g
             log(f"decode step eff {e}: {t:.1f} us, {gbs:.1f} GB/s")
         del ds

@@ -33,7 +33,7 @@ __all__ = [
     "rng_for", "f32_to_bf16_bits", "bf16_bits_to_f32", "fp16_bits",
     "gen_codes", "gen_scales", "gen_x_stream", "calibrate_theta", "make_linear",
     "small_case", "llama8b_linears", "llama8b_linears_b4", "llama8b_decode_step",
-    "llama70b_linears", "LLAMA8B_SHAPES", "LLAMA8B_LAYER", "LLAMA70B_SHAPES",
+    "llama70b_linears", "LLAMA8B_SHAPES", "LLAMA8B_FUSED_LAYER", "LLAMA70B_SHAPES",
     "torch_seed",
 ]
 
@@ -55,9 +55,11 @@ QUANTILES_B4 = {
 QUANTILES_SMALL = (0.20, 0.50, 0.80, 0.95)   # 20/30/30/15/5 %, mean ~3.1 bits
 
 LLAMA8B_SHAPES = ((4096, 4096), (4096, 14336), (14336, 4096))
-# one decoder layer: q, k, v, o, gate, up, down (d_in, d_out)
-LLAMA8B_LAYER = ((4096, 4096), (4096, 1024), (4096, 1024), (4096, 4096),
-                 (4096, 14336), (4096, 14336), (14336, 4096))
+# one decoder layer as decode launches it (d_in, d_out): q, k and v read the same
+# x and run as one fused q|k|v projection, gate and up likewise as gate|up;
+# o needs the attention output and down the activated gate|up output, so the
+# four run one after another
+LLAMA8B_FUSED_LAYER = ((4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096))
 LLAMA70B_SHAPES = ((8192, 8192), (8192, 28672), (28672, 8192))
 
 
@@ -198,12 +200,14 @@ def llama8b_linears_b4(eff_bits: float) -> list:
 
 
 def llama8b_decode_step(eff_bits: int, n_layers: int = 32) -> list:
-    """All 7 linears of every decoder layer, each with its own x and thresholds."""
+    """The projections of every decoder layer in launch order (fused q|k|v, o,
+    fused gate|up, down), each with its own x and thresholds; a fused
+    projection has one x and one threshold vector."""
     out = []
     for layer in range(n_layers):
-        for lin, (di, do) in enumerate(LLAMA8B_LAYER):
+        for lin, (di, do) in enumerate(LLAMA8B_FUSED_LAYER):
             out.append(LinearSpec(di, do, 8, "t3", "bf16", QUANTILES_B8[eff_bits],
-                                  key=(4, 0, layer, lin)))
+                                  key=(4, 1, layer, lin)))
     return out
 
 

@@ -325,9 +325,10 @@ def test_full_llama70b_linears(dev, eff):
 
 @pytest.mark.parametrize("eff,n_layers", [(3, 32), (2, 2), (4, 2), (6, 2), (8, 2)])
 def test_full_decode_step_sampled(dev, eff, n_layers):
-    """Every linear of the 32-layer 8B decode step (codes drawn on the device
-    from a seeded generator), 64 sampled outputs of each checked against the
-    oracle on the same code rows."""
+    """Every projection of the 32-layer 8B decode step as the benchmark
+    launches it (fused q|k|v 4096->6144, o, fused gate|up 4096->28672, down;
+    codes drawn on the device from a seeded generator), 64 sampled outputs of
+    each checked against the oracle on the same code rows."""
     import torch
     specs = S.llama8b_decode_step(eff, n_layers)
     say(f"decode step eff={eff} layers={n_layers} linears={len(specs)}")
