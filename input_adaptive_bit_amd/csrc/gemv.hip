@@ -99,14 +99,36 @@ __device__ __forceinline__ void accumulate(float (&acc)[16 * V], const uint32_t 
     }
 }
 
+static_assert(kWaves == 4, "one count byte per wave in a word");
+
 struct SliceLists {
     uint32_t off[kMaxChunk];   // byte offset of the channel's plane 0 row: i * P * row_bytes
     float xv[kMaxChunk];       // x_i * 4^(P - Pi): the multiplier of its Pi-plane code
-    int start[5];              // bucket Pi starts at start[Pi - 1] .. start[Pi]
-    int wave_cnt[4][kWaves];   // per-level wave counts
+    uint32_t cnt[4];           // word l, byte w: loaded channels of wave w with l + 1 planes
     float red_s[kWaves], red_c[kWaves];
     int is_last;
 };
+
+// Sum over the 64 lanes in a fixed order; every lane gets the total.  Lanes
+// i and i ^ 32, then rows r and r ^ 1 are added with the swap instructions,
+// then the 16 lanes of each row with DPP rotations and quad permutes.
+__device__ __forceinline__ float wave_sum(float v) {
+    {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        const uint32_t a = r[0], b = r[1];     // copied out before reinterpreting
+        v = __uint_as_float(a) + __uint_as_float(b);
+    }
+    {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        const uint32_t a = r[0], b = r[1];
+        v = __uint_as_float(a) + __uint_as_float(b);
+    }
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // lane ^ 2
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // lane ^ 1
+    return v;
+}
 
 // Plane words of U channels of one bucket (Pb planes each) of one worker.
 // x_i stays in LDS until the decode, so a batch holds only plane words.
@@ -172,9 +194,11 @@ struct Bucket {
     static constexpr int stride = kWaves * G;
     Batch<Pb, V, U> B;
     int e, end;
-    __device__ __forceinline__ void first(const SliceLists& L, int worker, const PlaneSrc& src) {
-        e = L.start[Pb - 1] + worker;
-        end = L.start[Pb];
+    // begin, end: the bucket's entries (wave-uniform)
+    __device__ __forceinline__ void first(const SliceLists& L, int begin, int end_, int worker,
+                                          const PlaneSrc& src) {
+        e = begin + worker;
+        end = end_;
         load_batch<P, Pb, V, U>(B, L, e, stride, end, src);
     }
     __device__ __forceinline__ void finish(float (&acc)[16 * V], const SliceLists& L, const PlaneSrc& src) {
@@ -204,7 +228,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     const int split = local / D.n_tiles;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wv = tid / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
 
     float th[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -224,31 +248,33 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     for (int l = 0; l < P; ++l) {
         const unsigned long long m = __ballot(pi == l + 1);
         if (pi == l + 1) rank = __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == 0) L.wave_cnt[l][wv] = __popcll(m);
+        if (lane == 0) reinterpret_cast<uint8_t*>(L.cnt)[4 * l + wv] = static_cast<uint8_t>(__popcll(m));
     }
     __syncthreads();
-    {
-        // every thread forms the bucket starts from the wave counts itself:
-        // bucket Pi = 1 first, each in wave then lane order
-        int pos = rank, acc_start = 0;
+    // Bucket bounds and this wave's place in each bucket, as wave-uniform
+    // scalars: bucket Pi = 1 first, each in wave then lane order.
+    int start[5];   // bucket Pi holds entries start[Pi - 1] .. start[Pi] - 1
+    int below[4];   // first entry of bucket l + 1 written by this wave
+    start[0] = 0;
 #pragma unroll
-        for (int l = 0; l < P; ++l) {
+    for (int l = 0; l < 4; ++l) {
+        if (l < P) {
+            const uint32_t c = __builtin_amdgcn_readfirstlane(L.cnt[l]);
+            const int c0 = c & 255, c1 = (c >> 8) & 255, c2 = (c >> 16) & 255, c3 = c >> 24;
+            below[l] = start[l] + (wv > 0 ? c0 : 0) + (wv > 1 ? c1 : 0) + (wv > 2 ? c2 : 0);
+            start[l + 1] = start[l] + c0 + c1 + c2 + c3;
+        } else {
+            below[l] = start[l];
+            start[l + 1] = start[l];
+        }
+    }
+    if (pi > 0) {
+        int pos = below[0];
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const int c = L.wave_cnt[l][w];
-                if (l < pi - 1 || (l == pi - 1 && w < wv)) pos += c;
-                acc_start += c;
-            }
-            if (tid == 0) L.start[l + 1] = acc_start;
-        }
-        if (tid == 0) {
-            L.start[0] = 0;
-            for (int l = P; l < 4; ++l) L.start[l + 1] = acc_start;
-        }
-        if (pi > 0) {
-            L.off[pos] = static_cast<uint32_t>(i0 + tid) * (P * static_cast<uint32_t>(D.row_words) * 4u);
-            L.xv[pos] = xv * static_cast<float>(1u << (2 * (P - pi)));
-        }
+        for (int l = 1; l < P; ++l) pos = pi == l + 1 ? below[l] : pos;
+        pos += rank;
+        L.off[pos] = static_cast<uint32_t>(i0 + tid) * (P * static_cast<uint32_t>(D.row_words) * 4u);
+        L.xv[pos] = xv * static_cast<float>(1u << (2 * (P - pi)));
     }
     __syncthreads();
 
@@ -274,33 +300,28 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     // then keeps a part of its loads in the CU's queue instead of all of
     // them, so the resident workgroups are served side by side rather than
     // one after another.
-    if constexpr (P >= 4) k4.first(L, worker, src);
-    if constexpr (P >= 3) k3.first(L, worker, src);
+    if constexpr (P >= 4) k4.first(L, start[3], start[4], worker, src);
+    if constexpr (P >= 3) k3.first(L, start[2], start[3], worker, src);
     if constexpr (P <= 2) {
-        if constexpr (P >= 2) k2.first(L, worker, src);
-        k1.first(L, worker, src);
+        if constexpr (P >= 2) k2.first(L, start[1], start[2], worker, src);
+        k1.first(L, start[0], start[1], worker, src);
     }
 
     // slice sums S and C over loaded channels (fixed-order reduction), while
     // the first plane loads are in flight
     {
-        float s_part = pi > 0 ? xv : 0.f;
-        float c_part = pi > 0 ? xv * phi_of(b_max, 2 * pi) : 0.f;
-#pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) {
-            s_part += __shfl_xor(s_part, off);
-            c_part += __shfl_xor(c_part, off);
-        }
+        const float s_w = wave_sum(pi > 0 ? xv : 0.f);
+        const float c_w = wave_sum(pi > 0 ? xv * phi_of(b_max, 2 * pi) : 0.f);
         if (lane == 0) {
-            L.red_s[wv] = s_part;
-            L.red_c[wv] = c_part;
+            L.red_s[wv] = s_w;
+            L.red_c[wv] = c_w;
         }
     }
     if constexpr (P >= 4) k4.finish(acc, L, src);
     if constexpr (P >= 3) {
-        k2.first(L, worker, src);
+        k2.first(L, start[1], start[2], worker, src);
         k3.finish(acc, L, src);
-        k1.first(L, worker, src);
+        k1.first(L, start[0], start[1], worker, src);
     }
     if constexpr (P >= 2) k2.finish(acc, L, src);
     k1.finish(acc, L, src);
