@@ -47,7 +47,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxChunk = kThreads;       // one channel per thread in the prologue
-constexpr int kMinChunk = 64;
 constexpr int kWgPerCu = 4;               // resident workgroups per CU the kernel is sized for
 constexpr int kV = 2;                     // plane words per lane per plane row (8-byte loads)
 
@@ -430,36 +429,27 @@ hipError_t launch_p(const GemvGroupArgs& a, int G, int total_wg, hipStream_t str
 int gemv_tile_outputs(int G) { return (kWave / G) * 16 * kV; }
 
 // Optional launch-shape overrides for tuning on new shapes:
-// GRINQH_LANE_GROUPS (1, 2, 4 or 8) and GRINQH_CHUNK (1 .. 256 channels).
+// GRINQH_LANE_GROUPS (1, 2, 4 or 8) and GRINQH_CHUNK (1 .. 256 channels per slice).
 int env_int(const char* name) {
     const char* v = std::getenv(name);
     return v ? std::atoi(v) : 0;
 }
 
-GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_groups, double launch_area) {
-    const int env_groups = env_int("GRINQH_LANE_GROUPS");
+GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_groups) {
+    (void)dev;
     const int env_chunk = env_int("GRINQH_CHUNK");
     GemvPlan pl{};
     const int padded = L.row_words * 16;
-    // Tile: 4 lane groups of 16 lanes, 512 outputs (128-byte plane-row
-    // segments per group); wide outputs use wider tiles to bound the tile count.
-    int G = 4;
-    if (padded >= 4096 * 7) G = 2;
-    if (env_groups == 1 || env_groups == 2 || env_groups == 4 || env_groups == 8) G = env_groups;
-    if (lane_groups == 1 || lane_groups == 2 || lane_groups == 4 || lane_groups == 8) G = lane_groups;
+    const int G = (lane_groups == 1 || lane_groups == 2 || lane_groups == 8) ? lane_groups : 4;
     pl.lane_groups = G;
     pl.tile_outputs = gemv_tile_outputs(G);
     pl.n_tiles = (padded + pl.tile_outputs - 1) / pl.tile_outputs;
-    // Slice length: one workgroup per (tile, slice), and about kWgPerCu
-    // workgroups per CU over the whole launch (all members of a group get
-    // the same slice length, so the work per workgroup is even).  That is a
-    // single generation of workgroups: each pays the prologue and the
-    // reduction tail once, and its loads overlap those of all the others.
-    const double area = launch_area > 0 ? launch_area : static_cast<double>(L.d_in) * padded;
-    const double target = static_cast<double>(kWgPerCu) * (dev.cu_count > 0 ? dev.cu_count : 256);
-    int chunk = static_cast<int>(area / (target * pl.tile_outputs) + 0.5);
-    if (chunk < kMinChunk) chunk = kMinChunk;
-    if (chunk > kMaxChunk) chunk = kMaxChunk;
+    // Slices as long as the prologue allows (one channel per thread): every
+    // split of a tile adds one more row of atomics and one more workgroup the
+    // tile's last arriver waits for, and the main loop of a slice is short
+    // next to that fixed chain, so fewer, longer slices are faster even when
+    // they leave CUs idle.
+    int chunk = kMaxChunk;
     if (env_chunk >= 1 && env_chunk <= kMaxChunk) chunk = env_chunk;
     int n_splits = (L.d_in + chunk - 1) / chunk;
     if (n_splits < 1) n_splits = 1;
@@ -472,10 +462,18 @@ GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_group
     return pl;
 }
 
-double launch_area(const grinqh_layout& L, int lane_groups) {
-    const int T = gemv_tile_outputs(lane_groups);
-    const int padded = L.row_words * 16;
-    return static_cast<double>(L.d_in) * static_cast<double>((padded + T - 1) / T) * T;
+int choose_lane_groups(const grinqh_layout* layouts, int n, const DeviceInfo& dev) {
+    const int env = env_int("GRINQH_LANE_GROUPS");
+    if (env == 1 || env == 2 || env == 4 || env == 8) return env;
+    const long cus = dev.cu_count > 0 ? dev.cu_count : 256;
+    long wg = 0;
+    for (int k = 0; k < n; ++k) {
+        const GemvPlan p = plan_gemv(layouts[k], dev, 4);
+        wg += static_cast<long>(p.n_tiles) * p.n_splits;
+    }
+    if (wg > kWgPerCu * cus) return 2;      // wider tiles: at most about kWgPerCu workgroups per CU
+    if (8 * wg < 5 * cus) return 8;         // narrower tiles: at least about 0.6 workgroups per CU
+    return 4;
 }
 
 void fill_desc(GemvDesc* g, const grinqh_layout& L, const GemvPlan& plan, const void* x, int x_dtype,

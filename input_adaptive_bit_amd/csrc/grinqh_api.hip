@@ -45,15 +45,6 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 // The common tile width of a group: the narrowest any member would pick.
-int group_lane_groups(const grinqh_layout* layouts, int n, const DeviceInfo& dev) {
-    int G = 1;
-    for (int k = 0; k < n; ++k) {
-        const int g = plan_gemv(layouts[k], dev).lane_groups;
-        if (g > G) G = g;
-    }
-    return G;
-}
-
 size_t group_ws_bytes(const grinqh_layout* layouts, int n, const DeviceInfo& dev, int G) {
     size_t total = 0;
     for (int k = 0; k < n; ++k) total += plan_gemv(layouts[k], dev, G).ws_bytes;
@@ -138,7 +129,7 @@ size_t grinqh_gemv_workspace_bytes(const grinqh_layout* L) {
     DeviceInfo dev;
     hipError_t e;
     if (!current_device_info(&dev, &e)) return 0;
-    return plan_gemv(*L, dev).ws_bytes;
+    return plan_gemv(*L, dev, choose_lane_groups(L, 1, dev)).ws_bytes;
 }
 
 grinqh_status grinqh_pack(const grinqh_layout* L, const uint8_t* q, uint32_t* planes,
@@ -191,7 +182,7 @@ grinqh_status grinqh_gemv(const grinqh_layout* L, const void* x, grinqh_dtype x_
     DeviceInfo dev;
     hipError_t e;
     if (!current_device_info(&dev, &e)) return map_error(e);
-    GemvPlan plan = plan_gemv(*L, dev);
+    GemvPlan plan = plan_gemv(*L, dev, choose_lane_groups(L, 1, dev));
     if (workspace_bytes < plan.ws_bytes) return GRINQH_ENOSPACE;
     return map_error(launch_gemv(*L, plan, x, x_dtype, theta, planes, s, z, y, y_dtype,
                                  workspace, static_cast<hipStream_t>(stream)));
@@ -204,7 +195,7 @@ size_t grinqh_gemv_group_workspace_bytes(const grinqh_layout* layouts, int32_t n
     DeviceInfo dev;
     hipError_t e;
     if (!current_device_info(&dev, &e)) return 0;
-    return group_ws_bytes(layouts, n, dev, group_lane_groups(layouts, n, dev));
+    return group_ws_bytes(layouts, n, dev, choose_lane_groups(layouts, n, dev));
 }
 
 grinqh_status grinqh_gemv_group(const grinqh_layout* layouts, const grinqh_gemv_operands* ops,
@@ -236,16 +227,14 @@ grinqh_status grinqh_gemv_group(const grinqh_layout* layouts, const grinqh_gemv_
     DeviceInfo dev;
     hipError_t e;
     if (!current_device_info(&dev, &e)) return map_error(e);
-    const int G = group_lane_groups(layouts, n, dev);
+    const int G = choose_lane_groups(layouts, n, dev);
     if (workspace_bytes < group_ws_bytes(layouts, n, dev, G)) return GRINQH_ENOSPACE;
     GemvGroupArgs args{};
     args.n = n;
     char* ws = static_cast<char*>(workspace);
     int wg = 0;
-    double area = 0;
-    for (int k = 0; k < n; ++k) area += launch_area(layouts[k], G);
     for (int k = 0; k < n; ++k) {
-        const GemvPlan plan = plan_gemv(layouts[k], dev, G, area);
+        const GemvPlan plan = plan_gemv(layouts[k], dev, G);
         fill_desc(&args.g[k], layouts[k], plan, ops[k].x, x_dtype, ops[k].theta, ops[k].planes, ops[k].s,
                   ops[k].z, ops[k].y, y_dtype, ws, wg);
         ws += plan.ws_bytes;

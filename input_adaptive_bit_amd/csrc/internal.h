@@ -58,13 +58,13 @@ struct GemvGroupArgs {
     int n;
 };
 
-// lane_groups = 0: the plan picks the tile width; otherwise it is forced.
-// launch_area: padded d_in x d_out summed over every GEMV of the launch (a
-// group); 0 for a launch of this GEMV alone.  It sets the slice length.
-GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_groups = 0,
-                   double launch_area = 0);
-// Padded d_in x d_out of one GEMV at a tile width, for launch_area.
-double launch_area(const grinqh_layout& L, int lane_groups);
+// Plan of one GEMV at a tile width of lane_groups (1, 2, 4 or 8) lane groups
+// per wave.
+GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_groups);
+// Tile width for one launch of these n GEMVs (a group, or n = 1): 4 lane
+// groups, 2 when that gives more than four workgroups per CU, 8 when it gives
+// too few workgroups to reach most CUs.  GRINQH_LANE_GROUPS overrides it.
+int choose_lane_groups(const grinqh_layout* layouts, int n, const DeviceInfo& dev);
 
 void fill_desc(GemvDesc* g, const grinqh_layout& L, const GemvPlan& plan, const void* x, int x_dtype,
                const float* theta, const uint32_t* planes, const uint16_t* s, const uint16_t* z,

@@ -176,6 +176,43 @@ def test_gemv_ragged_shapes(dev, b_max, d_in, d_out, x_dtype):
     _run_and_check(dl, x, x_dtype, theta, y_ref, f"{d_in}->{d_out} b{b_max}", dev)
 
 
+@pytest.mark.parametrize("lane_groups", [1, 2, 4, 8])
+@pytest.mark.parametrize("chunk", [7, 64, 256])
+def test_gemv_forced_launch_shapes(dev, monkeypatch, lane_groups, chunk):
+    """Every tile width (1, 2, 4 or 8 lane groups per wave) with a short, a
+    mid and the longest slice length, forced through the library's tuning
+    overrides, on shapes with several tiles and slices and ragged tails:
+    single calls and a group call against the oracle."""
+    import torch
+    import input_adaptive_bit_amd as G
+    monkeypatch.setenv("GRINQH_LANE_GROUPS", str(lane_groups))
+    monkeypatch.setenv("GRINQH_CHUNK", str(chunk))
+    rng = np.random.default_rng(lane_groups * 1000 + chunk)
+    members, ops, refs = [], [], []
+    for b_max, (d_in, d_out) in [(8, (1500, 2500)), (8, (513, 4100)), (8, (40, 70))]:
+        say(f"forced G={lane_groups} chunk={chunk} b_max={b_max} {d_in}->{d_out}")
+        q = rng.integers(0, 1 << b_max, size=(d_out, d_in), dtype=np.uint8)
+        s = rng.uniform(0.001, 0.01, d_out).astype(np.float16)
+        z = rng.normal(0, 0.01, d_out).astype(np.float16)
+        x = S.bf16_bits_to_f32(S.f32_to_bf16_bits(rng.standard_t(3, d_in).astype(np.float32)))
+        theta = np.sort(np.quantile(np.abs(x), np.linspace(0.2, 0.9, b_max // 2))).astype(np.float32)
+        dl = DeviceLinear(q, s, z, b_max, dev)
+        y_ref = C.gemv(x, theta, q, s, z, b_max)
+        _run_and_check(dl, x, "bf16", theta, y_ref, f"G{lane_groups} c{chunk} {d_in}->{d_out}", dev,
+                       check_bf16=False)
+        members.append(dl)
+        ops.append((to_dev_x(x, "bf16", dev), _theta_dev(theta, dev), dl.planes, dl.s, dl.z,
+                    torch.empty(d_out, dtype=torch.float32, device=dev)))
+        refs.append(y_ref)
+    layouts = [m.L for m in members]
+    ws = G.new_group_workspace(layouts, dev)
+    G.grinqh_gemv_group(layouts, ops, ws)
+    torch.cuda.synchronize()
+    for k, (o, ref) in enumerate(zip(ops, refs)):
+        err = O.max_rel_error(o[5].cpu().numpy(), ref)
+        assert err <= TOL_F32, (k, err)
+
+
 def test_gemv_dense_and_all_skipped(dev):
     import torch
     rng = np.random.default_rng(5)
