@@ -1,17 +1,19 @@
 // The decode GEMV of GRINQH (papernotes.org note, key designs 1-3) for gfx950.
 //
 // One launch computes one or several independent GEMVs (a "group", all with
-// the same b_max).  Work item = (GEMV, output tile of T outputs, slice of
-// `chunk` input channels); one 256-thread workgroup per item.  The slice
-// length is chosen from the whole launch so that all items are resident at
-// once (about four workgroups per CU): one generation of workgroups.
+// the same b_max).  Work item = (GEMV, output tile of T outputs, slice of up
+// to 256 input channels); one 256-thread workgroup per item, all items
+// resident at once (one generation of workgroups).  Slices are as long as
+// the prologue allows, and the tile width (lane groups per wave) follows the
+// launch's workgroup count (plan_gemv, choose_lane_groups).
 //
 // Prologue (key design 1).  The workgroup reads its slice of x, assigns
 // b_i = 2 * #{k : theta_k <= |x_i|} with exact fp32 compares and bucket-sorts
 // the loaded channels (b_i > 0) by plane count Pi = b_i / 2 into LDS, in
-// ascending channel order inside each bucket (wave ballots + prefix sums, so
-// the order - and with it the fp32 summation order - is fixed).  It also
-// forms the slice's S = sum x_i and C = sum x_i * phi_i over loaded channels.
+// ascending channel order inside each bucket (wave ballots; the bucket bounds
+// are summed from per-wave counts on the scalar unit), so the order - and
+// with it the fp32 summation order - is fixed.  It also forms the slice's
+// S = sum x_i and C = sum x_i * phi_i over loaded channels.
 //
 // Main loop (key design 2).  A wave is split into G lane groups of 64/G
 // lanes; lane r of a group owns 16*V consecutive outputs of the tile.  The
@@ -20,22 +22,23 @@
 // per plane, so a group reads T/4 contiguous bytes per plane row, and
 // untaken planes and skipped channels issue no memory request.  Every
 // channel in a bucket has the same plane count, so the lanes of a wave never
-// diverge.  The first batch of every bucket - sized to hold a typical
-// slice's share - is issued before any decoding, so a workgroup waits for
-// about one memory round trip.
+// diverge.  Load batches are sized to hold a typical slice's share of a
+// bucket, and two buckets are in flight at a time.
 //
-// Decode and accumulate (key design 3).  The Pi plane words of 16 outputs are
-// merged in integer registers into byte codes (decode.hpp), each byte is
-// converted with one v_cvt_f32_ubyte and accumulated with one fp32 FMA into
-// acc_j += x_i * 4^(P-Pi) * code.  With A_j = sum_i x_i * code_ij,
+// Decode and accumulate (key design 3).  The Pi plane words of 16 outputs
+// become 16 exact floats (decode.hpp: packed FP4 / FP8 conversions for one and
+// two planes, a SWAR merge into byte codes and v_cvt_f32_ubyte for three and
+// four), each accumulated with one fp32 FMA into acc_j += x_i * 4^(P-Pi) * code.
+// With A_j = sum_i x_i * code_ij,
 //   y_j = sum_i x_i * (s_j * (code_ij + phi_i) + z_j) = s_j * (A_j + C) + z_j * S.
 //
-// Reduction.  Lane groups are summed with cross-lane shuffles, waves through
-// LDS; the tile's partial A_j + C_slice is added with fp32 atomics into a
-// workspace row and S_slice into a per-tile slot.  A per-tile arrival counter
-// elects the last workgroup, which applies the epilogue
-// y_j = s_j * acc_j + z_j * S (bf16 output rounded to nearest even) and
-// clears its workspace row and counter for the next call.
+// Reduction.  Every worker stores its partial row to LDS and each thread sums
+// the workers' copies of its outputs in a fixed order; the tile's partial
+// A_j + C_slice is added with fp32 atomics into a workspace row and S_slice
+// into a per-tile slot.  A per-tile arrival counter elects the last
+// workgroup, which applies the epilogue y_j = s_j * acc_j + z_j * S (bf16
+// output rounded to nearest even) and clears its workspace row and counter
+// for the next call.
 #include <cstdlib>
 
 #include "decode.hpp"
