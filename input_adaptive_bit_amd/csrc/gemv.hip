@@ -50,6 +50,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxChunk = kThreads;       // one channel per thread in the prologue
+constexpr int kMinChunk = 64;             // shortest slice the launch shape picks by itself
 constexpr int kWgPerCu = 4;               // resident workgroups per CU the kernel is sized for
 constexpr int kV = 2;                     // plane words per lane per plane row (8-byte loads)
 
@@ -438,22 +439,14 @@ int env_int(const char* name) {
     return v ? std::atoi(v) : 0;
 }
 
-GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_groups) {
-    (void)dev;
-    const int env_chunk = env_int("GRINQH_CHUNK");
+GemvPlan plan_gemv(const grinqh_layout& L, const LaunchShape& shape) {
     GemvPlan pl{};
     const int padded = L.row_words * 16;
-    const int G = (lane_groups == 1 || lane_groups == 2 || lane_groups == 8) ? lane_groups : 4;
+    const int G = shape.lane_groups;
     pl.lane_groups = G;
     pl.tile_outputs = gemv_tile_outputs(G);
     pl.n_tiles = (padded + pl.tile_outputs - 1) / pl.tile_outputs;
-    // Slices as long as the prologue allows (one channel per thread): every
-    // split of a tile adds one more row of atomics and one more workgroup the
-    // tile's last arriver waits for, and the main loop of a slice is short
-    // next to that fixed chain, so fewer, longer slices are faster even when
-    // they leave CUs idle.
-    int chunk = kMaxChunk;
-    if (env_chunk >= 1 && env_chunk <= kMaxChunk) chunk = env_chunk;
+    const int chunk = shape.chunk < 1 ? 1 : shape.chunk > kMaxChunk ? kMaxChunk : shape.chunk;
     int n_splits = (L.d_in + chunk - 1) / chunk;
     if (n_splits < 1) n_splits = 1;
     pl.chunk = (L.d_in + n_splits - 1) / n_splits;       // balanced slices
@@ -465,18 +458,46 @@ GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_group
     return pl;
 }
 
-int choose_lane_groups(const grinqh_layout* layouts, int n, const DeviceInfo& dev) {
-    const int env = env_int("GRINQH_LANE_GROUPS");
-    if (env == 1 || env == 2 || env == 4 || env == 8) return env;
-    const long cus = dev.cu_count > 0 ? dev.cu_count : 256;
+namespace {
+
+// Workgroups of a launch of these GEMVs at a tile width and slice length.
+long launch_workgroups(const grinqh_layout* layouts, int n, int G, int chunk) {
     long wg = 0;
     for (int k = 0; k < n; ++k) {
-        const GemvPlan p = plan_gemv(layouts[k], dev, 4);
+        const GemvPlan p = plan_gemv(layouts[k], LaunchShape{G, chunk});
         wg += static_cast<long>(p.n_tiles) * p.n_splits;
     }
-    if (wg > kWgPerCu * cus) return 2;      // wider tiles: at most about kWgPerCu workgroups per CU
-    if (8 * wg < 5 * cus) return 8;         // narrower tiles: at least about 0.6 workgroups per CU
-    return 4;
+    return wg;
+}
+
+}  // namespace
+
+LaunchShape choose_launch(const grinqh_layout* layouts, int n, const DeviceInfo& dev) {
+    const long cus = dev.cu_count > 0 ? dev.cu_count : 256;
+    LaunchShape sh{4, kMaxChunk};
+    // Tile width.  Every split of a tile adds one more row of atomics and one
+    // more workgroup that the tile's last arriver waits for, and the main
+    // loop of a slice is short next to that fixed chain: slices are as long
+    // as the prologue allows (one channel per thread), and the tile width
+    // keeps the launch within one generation of at most kWgPerCu workgroups
+    // per CU (G = 2) or, for small launches, reaches more CUs (G = 8).
+    const long wg4 = launch_workgroups(layouts, n, 4, kMaxChunk);
+    if (wg4 > kWgPerCu * cus) sh.lane_groups = 2;
+    else if (8 * wg4 < 5 * cus) sh.lane_groups = 8;
+    const int env_groups = env_int("GRINQH_LANE_GROUPS");
+    if (env_groups == 1 || env_groups == 2 || env_groups == 4 || env_groups == 8) sh.lane_groups = env_groups;
+    // Slice length.  A launch of W workgroups leaves the CUs unevenly loaded
+    // unless W is a multiple of the CU count; shorten the slices (not below
+    // kMinChunk) until W reaches the next multiple, without passing it.
+    const long wmin = launch_workgroups(layouts, n, sh.lane_groups, kMaxChunk);
+    const long target = (wmin + cus - 1) / cus * cus;
+    for (int c = kMaxChunk - 1; c >= kMinChunk; --c) {
+        if (launch_workgroups(layouts, n, sh.lane_groups, c) > target) break;
+        sh.chunk = c;
+    }
+    const int env_chunk = env_int("GRINQH_CHUNK");
+    if (env_chunk >= 1 && env_chunk <= kMaxChunk) sh.chunk = env_chunk;
+    return sh;
 }
 
 void fill_desc(GemvDesc* g, const grinqh_layout& L, const GemvPlan& plan, const void* x, int x_dtype,

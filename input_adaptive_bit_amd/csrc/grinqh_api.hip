@@ -45,9 +45,9 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 // The common tile width of a group: the narrowest any member would pick.
-size_t group_ws_bytes(const grinqh_layout* layouts, int n, const DeviceInfo& dev, int G) {
+size_t group_ws_bytes(const grinqh_layout* layouts, int n, const LaunchShape& shape) {
     size_t total = 0;
-    for (int k = 0; k < n; ++k) total += plan_gemv(layouts[k], dev, G).ws_bytes;
+    for (int k = 0; k < n; ++k) total += plan_gemv(layouts[k], shape).ws_bytes;
     return total;
 }
 
@@ -129,7 +129,7 @@ size_t grinqh_gemv_workspace_bytes(const grinqh_layout* L) {
     DeviceInfo dev;
     hipError_t e;
     if (!current_device_info(&dev, &e)) return 0;
-    return plan_gemv(*L, dev, choose_lane_groups(L, 1, dev)).ws_bytes;
+    return plan_gemv(*L, choose_launch(L, 1, dev)).ws_bytes;
 }
 
 grinqh_status grinqh_pack(const grinqh_layout* L, const uint8_t* q, uint32_t* planes,
@@ -182,7 +182,7 @@ grinqh_status grinqh_gemv(const grinqh_layout* L, const void* x, grinqh_dtype x_
     DeviceInfo dev;
     hipError_t e;
     if (!current_device_info(&dev, &e)) return map_error(e);
-    GemvPlan plan = plan_gemv(*L, dev, choose_lane_groups(L, 1, dev));
+    GemvPlan plan = plan_gemv(*L, choose_launch(L, 1, dev));
     if (workspace_bytes < plan.ws_bytes) return GRINQH_ENOSPACE;
     return map_error(launch_gemv(*L, plan, x, x_dtype, theta, planes, s, z, y, y_dtype,
                                  workspace, static_cast<hipStream_t>(stream)));
@@ -195,7 +195,7 @@ size_t grinqh_gemv_group_workspace_bytes(const grinqh_layout* layouts, int32_t n
     DeviceInfo dev;
     hipError_t e;
     if (!current_device_info(&dev, &e)) return 0;
-    return group_ws_bytes(layouts, n, dev, choose_lane_groups(layouts, n, dev));
+    return group_ws_bytes(layouts, n, choose_launch(layouts, n, dev));
 }
 
 grinqh_status grinqh_gemv_group(const grinqh_layout* layouts, const grinqh_gemv_operands* ops,
@@ -227,20 +227,21 @@ grinqh_status grinqh_gemv_group(const grinqh_layout* layouts, const grinqh_gemv_
     DeviceInfo dev;
     hipError_t e;
     if (!current_device_info(&dev, &e)) return map_error(e);
-    const int G = choose_lane_groups(layouts, n, dev);
-    if (workspace_bytes < group_ws_bytes(layouts, n, dev, G)) return GRINQH_ENOSPACE;
+    const LaunchShape shape = choose_launch(layouts, n, dev);
+    if (workspace_bytes < group_ws_bytes(layouts, n, shape)) return GRINQH_ENOSPACE;
     GemvGroupArgs args{};
     args.n = n;
     char* ws = static_cast<char*>(workspace);
     int wg = 0;
     for (int k = 0; k < n; ++k) {
-        const GemvPlan plan = plan_gemv(layouts[k], dev, G);
+        const GemvPlan plan = plan_gemv(layouts[k], shape);
         fill_desc(&args.g[k], layouts[k], plan, ops[k].x, x_dtype, ops[k].theta, ops[k].planes, ops[k].s,
                   ops[k].z, ops[k].y, y_dtype, ws, wg);
         ws += plan.ws_bytes;
         wg += plan.n_tiles * plan.n_splits;
     }
-    return map_error(launch_gemv_group(layouts[0].n_planes, G, args, wg, static_cast<hipStream_t>(stream)));
+    return map_error(launch_gemv_group(layouts[0].n_planes, shape.lane_groups, args, wg,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 grinqh_status grinqh_debug_codes(const grinqh_layout* L, const uint8_t* bits,

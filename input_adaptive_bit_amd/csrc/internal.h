@@ -58,13 +58,21 @@ struct GemvGroupArgs {
     int n;
 };
 
-// Plan of one GEMV at a tile width of lane_groups (1, 2, 4 or 8) lane groups
-// per wave.
-GemvPlan plan_gemv(const grinqh_layout& L, const DeviceInfo& dev, int lane_groups);
-// Tile width for one launch of these n GEMVs (a group, or n = 1): 4 lane
-// groups, 2 when that gives more than four workgroups per CU, 8 when it gives
-// too few workgroups to reach most CUs.  GRINQH_LANE_GROUPS overrides it.
-int choose_lane_groups(const grinqh_layout* layouts, int n, const DeviceInfo& dev);
+// Launch shape shared by every GEMV of one launch: lane groups per wave
+// (tile width: 1, 2, 4 or 8) and the slice length in input channels.
+struct LaunchShape {
+    int lane_groups;
+    int chunk;
+};
+
+// Plan of one GEMV at a launch shape.
+GemvPlan plan_gemv(const grinqh_layout& L, const LaunchShape& shape);
+// Launch shape for one launch of these n GEMVs (a group, or n = 1): slices
+// of up to 256 channels, 4 lane groups per wave (2 when that gives more than
+// four workgroups per CU, 8 when it gives too few to reach most CUs), and
+// the slices shortened until the workgroup count reaches a multiple of the
+// CU count.  GRINQH_LANE_GROUPS and GRINQH_CHUNK override it.
+LaunchShape choose_launch(const grinqh_layout* layouts, int n, const DeviceInfo& dev);
 
 void fill_desc(GemvDesc* g, const grinqh_layout& L, const GemvPlan& plan, const void* x, int x_dtype,
                const float* theta, const uint32_t* planes, const uint16_t* s, const uint16_t* z,
