@@ -13,7 +13,8 @@ bracketed by device synchronisation and HIP events on the launch stream.
 Reported value: required bytes per second, where required bytes = taken
 2-bit planes (sum_i b_i * d_out / 8) + fp16 s and z (4 * d_out), summed over
 the step's GEMVs.  Also reported: the effective-bits sweep 2/3/4/8 (8 = all
-channels at b_max, the dense dequant GEMV of the same kernel), the whole
+channels at b_max, the dense dequant GEMV of the same kernel), the same step
+stored at b_max 6 (levels 0/2/4/6) at 2/3/4/6 effective bits, the whole
 32-layer decode step (128 launches in dependency order: per layer the fused
 q|k|v, o, fused gate|up and down projections; 7.0 GB of planes at b_max 8) at
 the same effective bits, and the plain fp64 C oracle timed on the host cores
@@ -233,6 +234,7 @@ def main() -> int:
     ap.add_argument("--eff", type=int, default=3, choices=[2, 3, 4, 8])
     ap.add_argument("--sweep-reps", type=int, default=64, help="launches per (eff, shape) sweep point")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-b6", action="store_true", help="skip the b_max 6 sweep")
     ap.add_argument("--no-decode-step", action="store_true",
                     help="skip the 32-layer decode-step measurement (7.0 GB of planes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -334,6 +336,33 @@ def main() -> int:
             sweep[str(e) if e != 8 else "8 (dense)"] = row
             log(f"sweep eff {e}: " + ", ".join(f"{k} {v['us']} us {v['GB/s']} GB/s" for k, v in row.items()))
 
+    sweep_b6 = {}
+    if not args.no_sweep and not args.no_b6:
+        # the same shapes stored at b_max 6 (levels 0/2/4/6): 0.75 bytes per weight
+        effs6 = {e: None for e in (2, 3, 4, 6)}
+        specs6 = {e: S.llama8b_linears_b6(e) for e in effs6}
+        n6 = max(1, math.ceil(2 * MALL_BYTES / (0.75 * set_bytes)))
+        shapes6 = [Shape(specs6[3][k], n6, dev, {e: specs6[e][k] for e in effs6}) for k in range(3)]
+        step6 = Step(shapes6, dev)
+        for e in effs6:
+            def run6(e=e):
+                for r in range(args.sweep_reps):
+                    step6.launch(r % n6, e)
+            g = capture(run6)
+            time_graph(g)
+            t = time_graph(g) * 1e3 / args.sweep_reps
+            req = sum(sh.req[e] for sh in shapes6)
+            row = {"step (3 linears, one launch)": {
+                "us": round(t, 3), "GB/s": round(req / t / 1e3, 1),
+                "frac_of_peak": round(req / t / 1e3 / HBM_PEAK_GBS, 4), "required_MB": round(req / 1e6, 3),
+                "eff_bits": round(float(np.sum([sh.bits[e].astype(np.int64).sum() * sh.d_out for sh in shapes6]) /
+                                        np.sum([sh.d_in * sh.d_out for sh in shapes6])), 4)}}
+            sweep_b6[str(e) if e != 6 else "6 (dense)"] = row
+            del g
+            log(f"sweep b_max 6 eff {e}: {t:.2f} us, {req / t / 1e3:.1f} GB/s")
+        del step6, shapes6
+        torch.cuda.empty_cache()
+
     decode_step = {}
     if not args.no_decode_step:
         del step
@@ -398,6 +427,7 @@ def main() -> int:
         },
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "sweep_b_max_6": sweep_b6,
         "decode_step_32_layers": decode_step,
     }
     print(json.dumps(out), flush=True)

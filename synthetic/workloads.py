@@ -29,10 +29,10 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "LinearSpec", "Linear", "QUANTILES_B8", "QUANTILES_B4", "QUANTILES_SMALL",
+    "LinearSpec", "Linear", "QUANTILES_B8", "QUANTILES_B6", "QUANTILES_B4", "QUANTILES_SMALL",
     "rng_for", "f32_to_bf16_bits", "bf16_bits_to_f32", "fp16_bits",
     "gen_codes", "gen_scales", "gen_x_stream", "calibrate_theta", "make_linear",
-    "small_case", "llama8b_linears", "llama8b_linears_b4", "llama8b_decode_step",
+    "small_case", "llama8b_linears", "llama8b_linears_b6", "llama8b_linears_b4", "llama8b_decode_step",
     "llama70b_linears", "LLAMA8B_SHAPES", "LLAMA8B_FUSED_LAYER", "LLAMA70B_SHAPES",
     "torch_seed",
 ]
@@ -45,6 +45,12 @@ QUANTILES_B8 = {
     4: (0.10, 0.35, 0.65, 0.90),   # 10/25/30/25/10
     6: (0.05, 0.10, 0.25, 0.60),   # 5/5/15/35/40
     8: None,                       # dense: every threshold 0 -> all b_max
+}
+QUANTILES_B6 = {
+    2: (0.30, 0.75, 0.95),         # shares 30/45/20/5 % of 0/2/4/6 bits
+    3: (0.20, 0.50, 0.80),         # 20/30/30/20
+    4: (0.10, 0.30, 0.60),         # 10/20/30/40
+    6: None,                       # dense
 }
 QUANTILES_B4 = {
     1.5: (0.40, 0.85),             # 40/45/15 % of 0/2/4 bits
@@ -189,6 +195,12 @@ def small_case() -> LinearSpec:
 def llama8b_linears(eff_bits: int) -> list:
     """Attention projection and MLP shapes of an 8B Llama, b_max 8, bf16 x ~ t(3)."""
     return [LinearSpec(di, do, 8, "t3", "bf16", QUANTILES_B8[eff_bits], key=(2, k, 0, 0))
+            for k, (di, do) in enumerate(LLAMA8B_SHAPES)]
+
+
+def llama8b_linears_b6(eff_bits: int) -> list:
+    """Same shapes with b_max 6 (levels 0/2/4/6); bf16 x ~ t(3)."""
+    return [LinearSpec(di, do, 6, "t3", "bf16", QUANTILES_B6[eff_bits], key=(7, k, 0, 0))
             for k, (di, do) in enumerate(LLAMA8B_SHAPES)]
 
 

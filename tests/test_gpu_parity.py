@@ -346,6 +346,12 @@ def test_full_llama8b_linears(dev, eff):
         _full_linear_check(spec, dev)
 
 
+@pytest.mark.parametrize("eff", [2, 3, 6])
+def test_full_llama8b_linears_b6(dev, eff):
+    for spec in S.llama8b_linears_b6(eff):
+        _full_linear_check(spec, dev)
+
+
 @pytest.mark.parametrize("eff", [1.5, 2, 3, 4])
 def test_full_llama8b_linears_b4(dev, eff):
     for spec in S.llama8b_linears_b4(eff):

@@ -331,6 +331,26 @@ def test_synthetic_thresholds_hit_target_bits():
         assert abs(O.eff_bits(O.assign_bits(Lx.x, Lx.theta, 8)) - eff) < 0.2
     Ld = S.make_linear(S.llama8b_linears(8)[0], with_codes=False)
     assert O.eff_bits(O.assign_bits(Ld.x, Ld.theta, 8)) == 8.0
+    for eff in (2, 3, 4):
+        spec = S.llama8b_linears_b6(eff)[0]
+        Lx = S.make_linear(spec, with_codes=False)
+        assert abs(O.eff_bits(O.assign_bits(Lx.x, Lx.theta, 6)) - eff) < 0.2
+    L6 = S.make_linear(S.llama8b_linears_b6(6)[0], with_codes=False)
+    assert O.eff_bits(O.assign_bits(L6.x, L6.theta, 6)) == 6.0
+
+
+@pytest.mark.parametrize("table,b_max", [(S.QUANTILES_B8, 8), (S.QUANTILES_B6, 6), (S.QUANTILES_B4, 4)])
+def test_quantile_tables_give_their_expected_bits(table, b_max):
+    """Each table's cumulative levels imply level shares whose mean bit width
+    is exactly the table key (None: every channel at b_max)."""
+    for eff, q in table.items():
+        if q is None:
+            assert eff == b_max
+            continue
+        assert len(q) == b_max // 2 and all(a < b for a, b in zip(q, q[1:]))
+        c = (0.0,) + tuple(q) + (1.0,)
+        shares = [c[i + 1] - c[i] for i in range(len(c) - 1)]
+        assert abs(sum(2 * i * sh for i, sh in enumerate(shares)) - eff) < 1e-12
 
 
 def test_max_rel_error_metric():
