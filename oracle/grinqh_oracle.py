@@ -32,6 +32,12 @@ its reason in the design notes):
   k = 0 (phi = 1/2; KD3 gives no exception).  A channel with b = 0
   contributes nothing (KD1: its weights are never loaded).
 * s and z are per output channel (fp16), widened exactly to fp64.
+* Threshold calibration (KD1 calibrates the thresholds offline on the
+  magnitudes of about 128 sample inputs).  The magnitudes |x| of all samples
+  are pooled and sorted ascending (NaN after +Inf); the threshold at level q
+  is the linear-interpolation quantile v[lo] + t * (v[hi] - v[lo]) with
+  h = (n - 1) * q, lo = floor(h), hi = min(lo + 1, n - 1), t = h - lo,
+  computed in fp64 and rounded once to fp32.
 
 Parity pins that hold this module to the page and to mathematics are in
 tests/test_oracle_pins.py; none of them retypes the formulas below.
@@ -49,6 +55,7 @@ __all__ = [
     "unpack_fragments", "truncated_codes", "codes_from_planes", "phi",
     "dequant", "gemv", "gemv_from_planes", "gemv_columns", "eff_bits",
     "required_bytes", "bias_table", "round_to_bf16", "max_rel_error",
+    "quantile_position", "calibrate_thresholds",
 ]
 
 
@@ -202,6 +209,37 @@ def gemv_from_planes(x, theta, planes, s, z, b_max: int, d_out: int) -> np.ndarr
 def gemv_columns(x, theta, q_rows, s_cols, z_cols, b_max: int) -> np.ndarray:
     """Outputs for a sample of output channels: q_rows is q[cols, :]."""
     return gemv(x, theta, q_rows, s_cols, z_cols, b_max)
+
+
+# --------------------------------------------------------------------------
+# KD1: threshold calibration (offline)
+# --------------------------------------------------------------------------
+
+def quantile_position(n: int, level: float):
+    """Where level q falls among n sorted values: (lo, hi, t) with
+    h = (n - 1) * q in fp64, lo = floor(h), hi = min(lo + 1, n - 1), t = h - lo."""
+    if n < 1:
+        raise ValueError("no values")
+    if not (0.0 <= level <= 1.0):
+        raise ValueError("quantile level outside [0, 1]")
+    h = float(n - 1) * float(level)
+    lo = int(math.floor(h))
+    hi = min(lo + 1, n - 1)
+    return lo, hi, h - lo
+
+
+def calibrate_thresholds(x_calib, levels) -> np.ndarray:
+    """KD1: the thresholds as quantiles of the pooled calibration magnitudes
+    (see the reading in the module notes).  x_calib: any shape, fp32 values
+    (bf16 inputs widened exactly); levels: one per threshold, in [0, 1]."""
+    mags = np.abs(np.asarray(x_calib, dtype=np.float32).ravel()).astype(np.float64)
+    v = np.sort(mags)                      # ascending, NaN last
+    out = np.empty(len(levels), dtype=np.float64)
+    for k, q in enumerate(levels):
+        lo, hi, t = quantile_position(v.size, q)
+        a, b = v[lo], v[hi]
+        out[k] = a + t * (b - a)           # two roundings in fp64, no fused multiply-add
+    return out.astype(np.float32)
 
 
 # --------------------------------------------------------------------------

@@ -23,6 +23,9 @@ def _pins(golden_dir):
         lambda: pins.test_dense_mode_is_plain_dot(8),
         lambda: pins.test_single_active_channel(),
         lambda: pins.test_factorised_form(4),
+        lambda: pins.test_calibration_matches_numpy_linear_quantile(1000),
+        lambda: pins.test_calibration_closed_forms(),
+        lambda: pins.test_calibration_ties_and_nan_order(),
     ]
 
 
@@ -79,7 +82,34 @@ def _mut_level_count_off_by_one(x, theta, b_max):
     return np.minimum(b + 2 * (b > 0), b_max).astype(np.uint8)
 
 
+_orig_qpos = O.quantile_position
+_orig_calib = O.calibrate_thresholds
+
+
+def _mut_quantile_index_n(n, level):
+    h = min(float(n) * float(level), float(n - 1))
+    lo = int(np.floor(h))
+    return lo, min(lo + 1, n - 1), h - lo
+
+
+def _mut_quantile_no_interpolation(n, level):
+    lo, hi, t = _orig_qpos(n, level)
+    return lo, hi, 0.0
+
+
+def _mut_calibration_signed(x_calib, levels):
+    v = np.sort(np.asarray(x_calib, dtype=np.float64).ravel())
+    out = []
+    for q in levels:
+        lo, hi, t = _orig_qpos(v.size, q)
+        out.append(v[lo] + t * (v[hi] - v[lo]))
+    return np.asarray(out).astype(np.float32)
+
+
 MUTATIONS = {
+    "quantile_index_uses_n": ("quantile_position", _mut_quantile_index_n),
+    "quantile_not_interpolated": ("quantile_position", _mut_quantile_no_interpolation),
+    "calibration_on_signed_values": ("calibrate_thresholds", _mut_calibration_signed),
     "phi_exponent_off_by_one": ("phi", _mut_phi_exponent),
     "phi_zero_at_b_max": ("phi", _mut_phi_zero_at_full),
     "ties_go_down": ("assign_bits", _mut_ties_down),

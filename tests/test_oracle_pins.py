@@ -370,3 +370,61 @@ def test_round_to_bf16_against_bit_arithmetic():
     got = O.round_to_bf16(vals)
     back = (got.astype(np.uint32) << 16).view(np.float32)
     assert back.tolist() == [1.0, 1.0, 1.015625, -3.0, 0.0]
+
+
+# ---------------------------------------------------- threshold calibration --
+
+@pytest.mark.parametrize("n", [1, 2, 3, 1000, 4096 * 3 + 7])
+def test_calibration_matches_numpy_linear_quantile(n):
+    """The calibration quantile is numpy's linear method (numpy.quantile), up
+    to one fp32 step where numpy interpolates from the upper value."""
+    rng = np.random.default_rng(n)
+    x = rng.standard_t(3, n).astype(np.float32)
+    levels = [0.0, 0.2, 0.5, 0.73, 0.9999, 1.0]
+    got = O.calibrate_thresholds(x, levels)
+    ref = np.quantile(np.abs(x).astype(np.float64), levels).astype(np.float32)
+    assert np.all(np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64)) <= 1)
+    assert np.mean(got == ref) >= 0.8
+
+
+def test_calibration_closed_forms():
+    # integer ramp 0..n-1: the quantile at q is (n - 1) q exactly (dyadic q)
+    n = 1025
+    v = np.arange(n, dtype=np.float32)
+    for q in (0.0, 0.25, 0.5, 0.625, 1.0):
+        assert O.calibrate_thresholds(v, [q])[0] == np.float32((n - 1) * q)
+    # two values: a + q (b - a)
+    assert O.calibrate_thresholds(np.array([2.0, -6.0], np.float32), [0.25])[0] == np.float32(3.0)
+    # constant data, signs and order do not matter
+    c = np.full(77, -1.5, np.float32)
+    assert np.all(O.calibrate_thresholds(c, [0.0, 0.3, 1.0]) == np.float32(1.5))
+    rng = np.random.default_rng(5)
+    x = rng.normal(size=500).astype(np.float32)
+    lv = [0.1, 0.5, 0.9]
+    assert np.array_equal(O.calibrate_thresholds(x, lv), O.calibrate_thresholds(-x[::-1], lv))
+    # the ends are the smallest and largest magnitudes
+    assert O.calibrate_thresholds(x, [0.0])[0] == np.min(np.abs(x))
+    assert O.calibrate_thresholds(x, [1.0])[0] == np.max(np.abs(x))
+
+
+def test_calibration_ties_and_nan_order():
+    # repeated values: any level inside a run of equal values returns that value
+    v = np.array([1, 1, 1, 1, 4, 4, 4, 4], np.float32)
+    assert O.calibrate_thresholds(v, [0.2, 0.4])[0] == 1.0
+    assert O.calibrate_thresholds(v, [0.8])[0] == 4.0
+    # NaN sorts after +Inf: low levels stay finite, the top level is NaN
+    w = np.array([np.nan, 1.0, 2.0, np.inf], np.float32)
+    got = O.calibrate_thresholds(w, [0.0, 0.5, 1.0])
+    assert got[0] == 1.0 and np.isnan(got[2])
+    assert got[1] == np.float32(2.0 + 0.5 * np.inf) or np.isinf(got[1])
+
+
+def test_harness_thresholds_are_the_calibration_quantiles():
+    """The synthetic harness's thresholds (numpy.quantile) agree with the
+    calibration definition to within one fp32 step."""
+    spec = S.llama8b_linears(3)[0]
+    xs, _ = S.gen_x_stream(spec)
+    calib = S.bf16_bits_to_f32(S.f32_to_bf16_bits(xs[:spec.n_calib]))
+    th_h = S.calibrate_theta(calib, S.QUANTILES_B8[3], 4)
+    th_o = O.calibrate_thresholds(calib, S.QUANTILES_B8[3])
+    assert np.all(np.abs(th_h.view(np.int32).astype(np.int64) - th_o.view(np.int32).astype(np.int64)) <= 1)
