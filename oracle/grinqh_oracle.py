@@ -37,7 +37,7 @@ its reason in the design notes):
   are pooled and sorted ascending (NaN after +Inf); the threshold at level q
   is the linear-interpolation quantile v[lo] + t * (v[hi] - v[lo]) with
   h = (n - 1) * q, lo = floor(h), hi = min(lo + 1, n - 1), t = h - lo,
-  computed in fp64 and rounded once to fp32.
+  computed in fp64 and rounded once to fp32; at t = 0 it is v[lo] itself.
 
 Parity pins that hold this module to the page and to mathematics are in
 tests/test_oracle_pins.py; none of them retypes the formulas below.
@@ -238,7 +238,9 @@ def calibrate_thresholds(x_calib, levels) -> np.ndarray:
     for k, q in enumerate(levels):
         lo, hi, t = quantile_position(v.size, q)
         a, b = v[lo], v[hi]
-        out[k] = a + t * (b - a)           # two roundings in fp64, no fused multiply-add
+        # two roundings in fp64, no fused multiply-add; a level that falls on
+        # a value (t = 0) returns that value, even next to an infinite one
+        out[k] = a if t == 0.0 else a + t * (b - a)
     return out.astype(np.float32)
 
 

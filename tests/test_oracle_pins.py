@@ -415,8 +415,10 @@ def test_calibration_ties_and_nan_order():
     # NaN sorts after +Inf: low levels stay finite, the top level is NaN
     w = np.array([np.nan, 1.0, 2.0, np.inf], np.float32)
     got = O.calibrate_thresholds(w, [0.0, 0.5, 1.0])
-    assert got[0] == 1.0 and np.isnan(got[2])
-    assert got[1] == np.float32(2.0 + 0.5 * np.inf) or np.isinf(got[1])
+    assert got[0] == 1.0 and np.isinf(got[1]) and np.isnan(got[2])
+    # a level that lands on a value returns it, also next to +Inf
+    assert O.calibrate_thresholds(np.array([1.0, 2.0, np.inf], np.float32), [0.5])[0] == 2.0
+    assert O.calibrate_thresholds(np.array([1.0, np.inf], np.float32), [1.0])[0] == np.inf
 
 
 def test_harness_thresholds_are_the_calibration_quantiles():
