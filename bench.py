@@ -17,8 +17,9 @@ channels at b_max, the dense dequant GEMV of the same kernel), the same step
 stored at b_max 6 (levels 0/2/4/6) at 2/3/4/6 effective bits, the whole
 32-layer decode step (128 launches in dependency order: per layer the fused
 q|k|v, o, fused gate|up and down projections; 7.0 GB of planes at b_max 8) at
-the same effective bits, and the plain fp64 C oracle timed on the host cores
-over a bounded sample.
+the same effective bits, the offline threshold calibration (exact quantiles of
+128 samples' |x|), and the plain fp64 C oracle timed on the host cores over a
+bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -363,6 +364,29 @@ def main() -> int:
         del step6, shapes6
         torch.cuda.empty_cache()
 
+    calibration = {}
+    if not args.no_sweep:
+        # offline threshold calibration: 128 samples of each input width, bf16
+        for d_in in (4096, 14336):
+            spec = S.LinearSpec(d_in, 4096, 8, "t3", "bf16", S.QUANTILES_B8[3], key=(2, 9, 0, d_in))
+            xs, _ = S.gen_x_stream(spec)
+            xc = torch.from_numpy(S.f32_to_bf16_bits(xs[:spec.n_calib]).view(np.int16).copy()).to(dev)
+            xc = xc.view(torch.bfloat16)
+            ws_c = torch.empty(G.grinqh_calibrate_workspace_bytes(), dtype=torch.uint8, device=dev)
+            th_c = torch.empty(4, dtype=torch.float32, device=dev)
+            lv = list(spec.quantiles)
+
+            def cal(reps=16):
+                for _ in range(reps):
+                    G.grinqh_calibrate_thresholds(xc, lv, th_c, ws_c)
+            g = capture(cal)
+            time_graph(g)
+            t = time_graph(g) * 1e3 / 16
+            calibration[f"{spec.n_calib}x{d_in} bf16"] = {
+                "values": int(xc.numel()), "us": round(t, 2), "GB/s": round(xc.numel() * 2 / t / 1e3, 1)}
+            del g
+            log(f"calibration {spec.n_calib}x{d_in}: {t:.1f} us")
+
     decode_step = {}
     if not args.no_decode_step:
         del step
@@ -428,6 +452,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "sweep": sweep,
         "sweep_b_max_6": sweep_b6,
+        "threshold_calibration": calibration,
         "decode_step_32_layers": decode_step,
     }
     print(json.dumps(out), flush=True)

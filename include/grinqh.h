@@ -173,6 +173,29 @@ grinqh_status grinqh_gemv_group(const grinqh_layout* layouts, const grinqh_gemv_
 grinqh_status grinqh_debug_codes(const grinqh_layout* L, const uint8_t* bits,
                                  const uint32_t* planes, uint8_t* codes, void* stream);
 
+/* ---- Threshold calibration (offline) ----------------------------------
+ *
+ * KD1 fixes the thresholds offline from the magnitudes of about 128 sample
+ * inputs of a layer.  This call computes them as quantiles of the pooled
+ * magnitudes: with the count magnitudes |x| sorted ascending (NaN after
+ * +Inf), for each level q, h = (count - 1) * q, lo = floor(h),
+ * hi = min(lo + 1, count - 1), t = h - lo,
+ *   theta = v[lo] + t * (v[hi] - v[lo])      (fp64; v[lo] itself at t = 0),
+ * rounded once to fp32.  The result is exact: order statistics by radix
+ * selection, no sampling.
+ *   x          count values (bf16 or fp32), e.g. n samples x d_in, any order.
+ *   count      1 .. 2^32 - 1.
+ *   levels     host array [n_levels] of quantile levels in [0, 1]; n_levels
+ *              1 .. 4 (one per threshold, ascending levels give ascending
+ *              thresholds).
+ *   theta      fp32 [n_levels] out.
+ *   workspace  >= grinqh_calibrate_workspace_bytes() bytes, 256-byte aligned;
+ *              any contents (the call initialises it). */
+size_t grinqh_calibrate_workspace_bytes(void);
+grinqh_status grinqh_calibrate_thresholds(const void* x, grinqh_dtype x_dtype, int64_t count,
+                                          const double* levels, int32_t n_levels, float* theta,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,4 +11,5 @@ from .grinqh import (  # noqa: F401
     grinqh_pack, grinqh_assign_bits, grinqh_gemv, grinqh_debug_codes,
     grinqh_gemv_group_workspace_bytes, grinqh_gemv_group, Operands, MAX_GROUP,
     new_workspace, new_group_workspace, pack, assign_bits, gemv, debug_codes,
+    grinqh_calibrate_workspace_bytes, grinqh_calibrate_thresholds, calibrate_thresholds,
 )

@@ -45,7 +45,8 @@ MAX_GROUP = 8
 
 EXPORTS = ("grinqh_version", "grinqh_status_string", "grinqh_layout_init", "grinqh_packed_bytes",
            "grinqh_gemv_workspace_bytes", "grinqh_pack", "grinqh_assign_bits", "grinqh_gemv",
-           "grinqh_gemv_group_workspace_bytes", "grinqh_gemv_group", "grinqh_debug_codes")
+           "grinqh_gemv_group_workspace_bytes", "grinqh_gemv_group", "grinqh_debug_codes",
+           "grinqh_calibrate_workspace_bytes", "grinqh_calibrate_thresholds")
 
 _lib = None
 
@@ -91,6 +92,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.grinqh_gemv_group.restype = ctypes.c_int
     lib.grinqh_debug_codes.argtypes = [LP, vp, vp, vp, vp]
     lib.grinqh_debug_codes.restype = ctypes.c_int
+    lib.grinqh_calibrate_workspace_bytes.argtypes = []
+    lib.grinqh_calibrate_workspace_bytes.restype = sz
+    lib.grinqh_calibrate_thresholds.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_double),
+                                                i32, vp, vp, sz, vp]
+    lib.grinqh_calibrate_thresholds.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -237,6 +243,25 @@ def grinqh_debug_codes(L: Layout, bits, planes, codes, stream=None) -> None:
            "grinqh_debug_codes")
 
 
+def grinqh_calibrate_workspace_bytes() -> int:
+    return int(load().grinqh_calibrate_workspace_bytes())
+
+
+def grinqh_calibrate_thresholds(x, levels, theta, workspace, stream=None) -> None:
+    """Thresholds as quantiles of the pooled |x| (x: bf16 or fp32 tensor of any
+    shape, contiguous; levels: host sequence of 1..4 levels in [0, 1];
+    theta: fp32 tensor [len(levels)])."""
+    import torch
+    _need(x, "x", (torch.bfloat16, torch.float32), None)
+    lv = (ctypes.c_double * len(levels))(*[float(q) for q in levels])
+    _need(theta, "theta", (torch.float32,), 4 * len(levels))
+    _need(workspace, "workspace", None)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().grinqh_calibrate_thresholds(_ptr(x), _dtype_code(x), x.numel(), lv, len(levels), _ptr(theta),
+                                              _ptr(workspace), ws_bytes, _stream(stream)),
+           "grinqh_calibrate_thresholds")
+
+
 # ------------------------------------------------- allocating conveniences --
 
 def new_workspace(L: Layout, device=None):
@@ -283,6 +308,17 @@ def gemv(L: Layout, x, theta, planes, s, z, workspace=None, out_dtype=None, stre
     y = torch.empty(L.d_out, dtype=out_dtype or torch.float32, device=x.device)
     grinqh_gemv(L, x, theta, planes, s, z, y, workspace, stream)
     return y
+
+
+def calibrate_thresholds(x, levels, workspace=None, stream=None):
+    """fp32 thresholds [len(levels)] on x's device (allocates theta and, if not
+    given, the workspace)."""
+    import torch
+    if workspace is None:
+        workspace = torch.empty(grinqh_calibrate_workspace_bytes(), dtype=torch.uint8, device=x.device)
+    theta = torch.empty(len(levels), dtype=torch.float32, device=x.device)
+    grinqh_calibrate_thresholds(x, levels, theta, workspace, stream)
+    return theta
 
 
 def debug_codes(L: Layout, bits, planes, stream=None):

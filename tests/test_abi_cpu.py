@@ -160,3 +160,34 @@ def test_group_argument_checks_before_any_device_call():
     assert call(o=o5) == B.GRINQH_EINVAL
     assert lib.grinqh_gemv_group_workspace_bytes(bad, 2) == 0
     assert lib.grinqh_gemv_group_workspace_bytes(arr, 0) == 0
+
+
+def test_calibration_argument_checks_before_any_device_call():
+    lib = G.load()
+    A = 1 << 16
+    X, TH, WS = A, 2 * A, 3 * A
+    wsb = lib.grinqh_calibrate_workspace_bytes()
+    assert wsb >= 8 * 2048 * 4 and wsb % 256 == 0
+
+    def call(x=X, xd=0, n=1000, levels=(0.2, 0.5), nl=None, th=TH, ws=WS, b=wsb):
+        lv = (ctypes.c_double * max(1, len(levels)))(*levels)
+        return lib.grinqh_calibrate_thresholds(x, xd, n, lv, len(levels) if nl is None else nl, th, ws, b, None)
+
+    assert call(x=None) == B.GRINQH_EINVAL
+    assert call(th=None) == B.GRINQH_EINVAL
+    assert call(ws=None) == B.GRINQH_EINVAL
+    assert lib.grinqh_calibrate_thresholds(X, 0, 10, None, 1, TH, WS, wsb, None) == B.GRINQH_EINVAL
+    assert call(xd=2) == B.GRINQH_EINVAL
+    assert call(n=0) == B.GRINQH_EINVAL
+    assert call(n=-5) == B.GRINQH_EINVAL
+    assert call(n=1 << 32) == B.GRINQH_EINVAL
+    assert call(levels=(), nl=0) == B.GRINQH_EINVAL
+    assert call(levels=(0.1, 0.2, 0.3, 0.4, 0.5)) == B.GRINQH_EINVAL
+    assert call(levels=(0.2, 1.5)) == B.GRINQH_EINVAL
+    assert call(levels=(-0.01,)) == B.GRINQH_EINVAL
+    assert call(levels=(float("nan"),)) == B.GRINQH_EINVAL
+    assert call(x=X + 1) == B.GRINQH_EALIGN
+    assert call(xd=1, x=X + 2) == B.GRINQH_EALIGN
+    assert call(th=TH + 2) == B.GRINQH_EALIGN
+    assert call(ws=WS + 64) == B.GRINQH_EALIGN
+    assert call(b=wsb - 1) == B.GRINQH_ENOSPACE
