@@ -38,6 +38,15 @@ its reason in the design notes):
   is the linear-interpolation quantile v[lo] + t * (v[hi] - v[lo]) with
   h = (n - 1) * q, lo = floor(h), hi = min(lo + 1, n - 1), t = h - lo,
   computed in fp64 and rounded once to fp32; at t = 0 it is v[lo] itself.
+* Offline quantisation ("RTN", named by the page as a base the method can
+  sit on, not defined there).  Per output channel j, asymmetric
+  round-to-nearest onto the b_max-bit grid of interval midpoints that the
+  KD3 dequantisation reconstructs at b = b_max: lo_j and hi_j are the row's
+  minimum and maximum (NaN ignored), s_j = fp16((hi_j - lo_j) / 2^b_max),
+  z_j = fp16(lo_j), and q = min(max(floor((w - z_j) / s_j), 0), 2^b_max - 1)
+  in fp32 with the stored s_j and z_j (a NaN quotient gives 0; a row with
+  s_j = 0 gets q = 0).  Then s_j * (q + 1/2) + z_j is the midpoint of w's
+  interval, within s_j / 2 of w.
 
 Parity pins that hold this module to the page and to mathematics are in
 tests/test_oracle_pins.py; none of them retypes the formulas below.
@@ -55,7 +64,7 @@ __all__ = [
     "unpack_fragments", "truncated_codes", "codes_from_planes", "phi",
     "dequant", "gemv", "gemv_from_planes", "gemv_columns", "eff_bits",
     "required_bytes", "bias_table", "round_to_bf16", "max_rel_error",
-    "quantile_position", "calibrate_thresholds",
+    "quantile_position", "calibrate_thresholds", "quantize_rtn",
 ]
 
 
@@ -242,6 +251,31 @@ def calibrate_thresholds(x_calib, levels) -> np.ndarray:
         # a value (t = 0) returns that value, even next to an infinite one
         out[k] = a if t == 0.0 else a + t * (b - a)
     return out.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Offline quantisation front end (RTN onto the KD3 midpoint grid)
+# --------------------------------------------------------------------------
+
+def quantize_rtn(w, b_max: int):
+    """Codes, scales and zero points of a weight matrix w [d_out][d_in]
+    (fp32 values, e.g. widened from bf16) at b_max bits; see the reading in
+    the module notes.  Returns (q uint8 [d_out][d_in], s fp16 [d_out],
+    z fp16 [d_out]).  All arithmetic in fp32, as the reading fixes it."""
+    w = np.asarray(w, dtype=np.float32)
+    levels = np.float32(1 << b_max)
+    lo = np.fmin.reduce(w, axis=1)                     # NaN ignored
+    hi = np.fmax.reduce(w, axis=1)
+    s = ((hi - lo) / levels).astype(np.float16)
+    z = lo.astype(np.float16)
+    s32 = s.astype(np.float32)[:, None]
+    z32 = z.astype(np.float32)[:, None]
+    with np.errstate(invalid="ignore", divide="ignore"):
+        u = np.floor((w - z32) / s32)
+    u = np.where(np.isnan(u), np.float32(0), u)
+    u = np.minimum(np.maximum(u, np.float32(0)), levels - np.float32(1))
+    u = np.where(s32 == 0, np.float32(0), u)
+    return u.astype(np.uint8), s, z
 
 
 # --------------------------------------------------------------------------

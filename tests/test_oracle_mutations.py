@@ -26,6 +26,10 @@ def _pins(golden_dir):
         lambda: pins.test_calibration_matches_numpy_linear_quantile(1000),
         lambda: pins.test_calibration_closed_forms(),
         lambda: pins.test_calibration_ties_and_nan_order(),
+        lambda: pins.test_rtn_codes_on_an_exact_integer_grid(3),
+        lambda: pins.test_rtn_codes_at_interval_centres(),
+        lambda: pins.test_rtn_round_trip_bound(8),
+        lambda: pins.test_rtn_special_rows(),
     ]
 
 
@@ -106,7 +110,32 @@ def _mut_calibration_signed(x_calib, levels):
     return np.asarray(out).astype(np.float32)
 
 
+_orig_rtn = O.quantize_rtn
+
+
+def _mut_rtn_scale_minus_one(w, b_max):
+    w = np.asarray(w, np.float32)
+    lo, hi = np.fmin.reduce(w, axis=1), np.fmax.reduce(w, axis=1)
+    s = ((hi - lo) / np.float32((1 << b_max) - 1)).astype(np.float16)
+    z = lo.astype(np.float16)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        u = np.floor((w - z.astype(np.float32)[:, None]) / s.astype(np.float32)[:, None])
+    u = np.clip(np.nan_to_num(u, nan=0.0), 0, (1 << b_max) - 1)
+    return u.astype(np.uint8), s, z
+
+
+def _mut_rtn_round_not_floor(w, b_max):
+    q, s, z = _orig_rtn(w, b_max)
+    w = np.asarray(w, np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        u = np.rint((w - z.astype(np.float32)[:, None]) / s.astype(np.float32)[:, None])
+    u = np.clip(np.nan_to_num(u, nan=0.0), 0, (1 << b_max) - 1)
+    return u.astype(np.uint8), s, z
+
+
 MUTATIONS = {
+    "rtn_scale_uses_levels_minus_one": ("quantize_rtn", _mut_rtn_scale_minus_one),
+    "rtn_rounds_instead_of_floor": ("quantize_rtn", _mut_rtn_round_not_floor),
     "quantile_index_uses_n": ("quantile_position", _mut_quantile_index_n),
     "quantile_not_interpolated": ("quantile_position", _mut_quantile_no_interpolation),
     "calibration_on_signed_values": ("calibrate_thresholds", _mut_calibration_signed),

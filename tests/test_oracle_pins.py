@@ -430,3 +430,69 @@ def test_harness_thresholds_are_the_calibration_quantiles():
     th_h = S.calibrate_theta(calib, S.QUANTILES_B8[3], 4)
     th_o = O.calibrate_thresholds(calib, S.QUANTILES_B8[3])
     assert np.all(np.abs(th_h.view(np.int32).astype(np.int64) - th_o.view(np.int32).astype(np.int64)) <= 1)
+
+
+# ------------------------------------------------------------ RTN front end --
+
+@pytest.mark.parametrize("k", [0, 3, 9])
+def test_rtn_codes_on_an_exact_integer_grid(k):
+    """b_max 8: rows of grid points w = q * 2^-k (exact in bf16) with a 0 and a
+    256 * 2^-k anchor have s = 2^-k, z = 0, and return their own q; the top
+    anchor is clamped to 255."""
+    rng = np.random.default_rng(k)
+    q_true = rng.integers(0, 256, size=(6, 300))
+    w = (q_true * 2.0 ** -k).astype(np.float32)
+    w[:, 0] = 0.0
+    w[:, 1] = 256 * 2.0 ** -k
+    q_true[:, 0] = 0
+    q_true[:, 1] = 255
+    q, s, z = O.quantize_rtn(w, 8)
+    assert np.all(s == np.float16(2.0 ** -k)) and np.all(z == 0)
+    assert np.array_equal(q, q_true.astype(np.uint8))
+
+
+def test_rtn_codes_at_interval_centres():
+    """b_max 4: rows of interval centres w = (q + 1/2) * 2^-3 with 0 and 2 as
+    anchors return q (a centre is never rounded up)."""
+    rng = np.random.default_rng(4)
+    q_true = rng.integers(0, 16, size=(5, 200))
+    w = ((q_true + 0.5) * 0.125).astype(np.float32)
+    w[:, 0], w[:, 1] = 0.0, 2.0
+    q_true[:, 0], q_true[:, 1] = 0, 15
+    q, s, z = O.quantize_rtn(w, 4)
+    assert np.all(s == np.float16(0.125)) and np.all(z == 0)
+    assert np.array_equal(q, q_true.astype(np.uint8))
+
+
+@pytest.mark.parametrize("b_max", [2, 4, 6, 8])
+def test_rtn_round_trip_bound(b_max):
+    """Every weight is within half an interval of its midpoint reconstruction,
+    up to the fp16 rounding of the stored scale and zero point."""
+    rng = np.random.default_rng(b_max)
+    w = rng.normal(0, 0.02, size=(64, 777)).astype(np.float32)
+    w[::7, 5] *= 40.0                                    # outliers
+    w = S.bf16_bits_to_f32(S.f32_to_bf16_bits(w))
+    q, s, z = O.quantize_rtn(w, b_max)
+    s64, z64 = s.astype(np.float64)[:, None], z.astype(np.float64)[:, None]
+    w_hat = s64 * (q.astype(np.float64) + 0.5) + z64
+    lo, hi = w.min(axis=1).astype(np.float64)[:, None], w.max(axis=1).astype(np.float64)[:, None]
+    s_exact = (hi - lo) / 2.0 ** b_max
+    bound = 0.5 * s64 + np.abs(z64 - lo) + 2.0 ** b_max * np.abs(s_exact - s64) + 1e-12
+    assert np.all(np.abs(w_hat - w) <= bound)
+    # and mostly within the half interval itself
+    assert np.mean(np.abs(w_hat - w) <= 0.5 * s64 * (1 + 1e-6)) > 0.98
+    # codes never decrease as the weight grows
+    for j in range(0, 64, 9):
+        o = np.argsort(w[j], kind="stable")
+        assert np.all(np.diff(q[j][o].astype(np.int64)) >= 0)
+
+
+def test_rtn_special_rows():
+    w = np.array([[1.5] * 8,                                           # constant
+                  [np.nan, 1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0],        # NaN ignored in min / max
+                  [0.0, 1.0, np.inf, 2.0, 3.0, 4.0, 5.0, 6.0]], np.float32)
+    q, s, z = O.quantize_rtn(w, 4)
+    assert s[0] == 0 and z[0] == np.float16(1.5) and np.all(q[0] == 0)
+    assert z[1] == 1.0 and s[1] == np.float16(6.0 / 16) and q[1, 0] == 0
+    assert q[1, 7] == 15 and q[1, 1] == 0
+    assert np.isinf(s[2]) and np.all(q[2] == 0)
