@@ -18,8 +18,8 @@ stored at b_max 6 (levels 0/2/4/6) at 2/3/4/6 effective bits, the whole
 32-layer decode step (128 launches in dependency order: per layer the fused
 q|k|v, o, fused gate|up and down projections; 7.0 GB of planes at b_max 8) at
 the same effective bits, the offline threshold calibration (exact quantiles of
-128 samples' |x|), and the plain fp64 C oracle timed on the host cores over a
-bounded sample.
+128 samples' |x|) and RTN quantisation (bf16 weights to b_max 8 codes), and the
+plain fp64 C oracle timed on the host cores over a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -387,6 +387,28 @@ def main() -> int:
             del g
             log(f"calibration {spec.n_calib}x{d_in}: {t:.1f} us")
 
+    rtn = {}
+    if not args.no_sweep:
+        # offline RTN quantisation of bf16 weights (reads 2 bytes and writes 1 per weight)
+        for di, do in S.LLAMA8B_SHAPES:
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(S.torch_seed((2, 8, di, do), 0))
+            wt = (torch.randn((do, di), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+            qt = torch.empty((do, di), dtype=torch.uint8, device=dev)
+            st_ = torch.empty(do, dtype=torch.float16, device=dev)
+            zt = torch.empty(do, dtype=torch.float16, device=dev)
+
+            def quant(reps=8):
+                for _ in range(reps):
+                    G.grinqh_quantize_rtn(wt, 8, qt, st_, zt)
+            g = capture(quant)
+            time_graph(g)
+            t = time_graph(g) * 1e3 / 8
+            moved = 3.0 * di * do
+            rtn[f"{di}x{do}"] = {"us": round(t, 2), "GB/s": round(moved / t / 1e3, 1)}
+            del g, wt, qt
+            log(f"rtn {di}x{do}: {t:.1f} us, {moved / t / 1e3:.1f} GB/s")
+
     decode_step = {}
     if not args.no_decode_step:
         del step
@@ -453,6 +475,7 @@ def main() -> int:
         "sweep": sweep,
         "sweep_b_max_6": sweep_b6,
         "threshold_calibration": calibration,
+        "rtn_quantisation_b_max_8": rtn,
         "decode_step_32_layers": decode_step,
     }
     print(json.dumps(out), flush=True)

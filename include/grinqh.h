@@ -196,6 +196,26 @@ grinqh_status grinqh_calibrate_thresholds(const void* x, grinqh_dtype x_dtype, i
                                           const double* levels, int32_t n_levels, float* theta,
                                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Offline quantisation front end ("RTN") ----------------------------
+ *
+ * The note names round-to-nearest (RTN) as a base the method can sit on
+ * without defining it.  This call quantises a bf16 weight matrix per output
+ * channel onto the b_max-bit grid whose KD3 reconstruction at b = b_max,
+ * s_j * (q + 1/2) + z_j, is the midpoint of each interval:
+ *   lo_j, hi_j = min and max of row j (NaN ignored);
+ *   s_j = fp16((hi_j - lo_j) / 2^b_max), z_j = fp16(lo_j) (zeros stored as +0);
+ *   q = min(max(floor((w - z_j) / s_j), 0), 2^b_max - 1), in fp32 with the
+ *       stored s_j and z_j (IEEE division; a NaN quotient gives 0, a row
+ *       with s_j = 0 gets 0).
+ * Every weight is then within s_j / 2 of its reconstruction, up to the fp16
+ * rounding of s_j and z_j.  The outputs feed grinqh_pack and grinqh_gemv.
+ *   w     bf16 [d_out][d_in]: row j holds output channel j's weights.
+ *   q     uint8 [d_out][d_in] out.
+ *   s, z  fp16 [d_out] out.
+ * d_in >= 1, 1 <= d_out <= 2^30, b_max in {2, 4, 6, 8}. */
+grinqh_status grinqh_quantize_rtn(int32_t d_in, int32_t d_out, int32_t b_max, const uint16_t* w,
+                                  uint8_t* q, uint16_t* s, uint16_t* z, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,4 +12,5 @@ from .grinqh import (  # noqa: F401
     grinqh_gemv_group_workspace_bytes, grinqh_gemv_group, Operands, MAX_GROUP,
     new_workspace, new_group_workspace, pack, assign_bits, gemv, debug_codes,
     grinqh_calibrate_workspace_bytes, grinqh_calibrate_thresholds, calibrate_thresholds,
+    grinqh_quantize_rtn, quantize_rtn,
 )

@@ -46,7 +46,7 @@ MAX_GROUP = 8
 EXPORTS = ("grinqh_version", "grinqh_status_string", "grinqh_layout_init", "grinqh_packed_bytes",
            "grinqh_gemv_workspace_bytes", "grinqh_pack", "grinqh_assign_bits", "grinqh_gemv",
            "grinqh_gemv_group_workspace_bytes", "grinqh_gemv_group", "grinqh_debug_codes",
-           "grinqh_calibrate_workspace_bytes", "grinqh_calibrate_thresholds")
+           "grinqh_calibrate_workspace_bytes", "grinqh_calibrate_thresholds", "grinqh_quantize_rtn")
 
 _lib = None
 
@@ -97,6 +97,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.grinqh_calibrate_thresholds.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_double),
                                                 i32, vp, vp, sz, vp]
     lib.grinqh_calibrate_thresholds.restype = ctypes.c_int
+    lib.grinqh_quantize_rtn.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.grinqh_quantize_rtn.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -262,6 +264,21 @@ def grinqh_calibrate_thresholds(x, levels, theta, workspace, stream=None) -> Non
            "grinqh_calibrate_thresholds")
 
 
+def grinqh_quantize_rtn(w, b_max: int, q, s, z, stream=None) -> None:
+    """RTN codes (uint8 [d_out][d_in]), scales and zero points (fp16 [d_out])
+    of a bf16 weight matrix w [d_out][d_in]."""
+    import torch
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [d_out][d_in]")
+    d_out, d_in = w.shape
+    _need(w, "w", (torch.bfloat16,), None)
+    _need(q, "q", (torch.uint8,), d_out * d_in)
+    _need(s, "s", (torch.float16,), 2 * d_out)
+    _need(z, "z", (torch.float16,), 2 * d_out)
+    _check(load().grinqh_quantize_rtn(d_in, d_out, int(b_max), _ptr(w), _ptr(q), _ptr(s), _ptr(z), _stream(stream)),
+           "grinqh_quantize_rtn")
+
+
 # ------------------------------------------------- allocating conveniences --
 
 def new_workspace(L: Layout, device=None):
@@ -319,6 +336,17 @@ def calibrate_thresholds(x, levels, workspace=None, stream=None):
     theta = torch.empty(len(levels), dtype=torch.float32, device=x.device)
     grinqh_calibrate_thresholds(x, levels, theta, workspace, stream)
     return theta
+
+
+def quantize_rtn(w, b_max: int, stream=None):
+    """(q, s, z) of a bf16 weight matrix on its device (allocates them)."""
+    import torch
+    d_out, d_in = w.shape
+    q = torch.empty((d_out, d_in), dtype=torch.uint8, device=w.device)
+    s = torch.empty(d_out, dtype=torch.float16, device=w.device)
+    z = torch.empty(d_out, dtype=torch.float16, device=w.device)
+    grinqh_quantize_rtn(w, b_max, q, s, z, stream)
+    return q, s, z
 
 
 def debug_codes(L: Layout, bits, planes, stream=None):

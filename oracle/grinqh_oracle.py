@@ -43,7 +43,7 @@ its reason in the design notes):
   round-to-nearest onto the b_max-bit grid of interval midpoints that the
   KD3 dequantisation reconstructs at b = b_max: lo_j and hi_j are the row's
   minimum and maximum (NaN ignored), s_j = fp16((hi_j - lo_j) / 2^b_max),
-  z_j = fp16(lo_j), and q = min(max(floor((w - z_j) / s_j), 0), 2^b_max - 1)
+  z_j = fp16(lo_j) (a zero stored as +0), and q = min(max(floor((w - z_j) / s_j), 0), 2^b_max - 1)
   in fp32 with the stored s_j and z_j (a NaN quotient gives 0; a row with
   s_j = 0 gets q = 0).  Then s_j * (q + 1/2) + z_j is the midpoint of w's
   interval, within s_j / 2 of w.
@@ -266,8 +266,9 @@ def quantize_rtn(w, b_max: int):
     levels = np.float32(1 << b_max)
     lo = np.fmin.reduce(w, axis=1)                     # NaN ignored
     hi = np.fmax.reduce(w, axis=1)
-    s = ((hi - lo) / levels).astype(np.float16)
-    z = lo.astype(np.float16)
+    # "+ 0" turns a -0 into +0, so the stored s and z have one zero
+    s = ((hi - lo) / levels + np.float32(0)).astype(np.float16)
+    z = (lo + np.float32(0)).astype(np.float16)
     s32 = s.astype(np.float32)[:, None]
     z32 = z.astype(np.float32)[:, None]
     with np.errstate(invalid="ignore", divide="ignore"):

@@ -191,3 +191,20 @@ def test_calibration_argument_checks_before_any_device_call():
     assert call(th=TH + 2) == B.GRINQH_EALIGN
     assert call(ws=WS + 64) == B.GRINQH_EALIGN
     assert call(b=wsb - 1) == B.GRINQH_ENOSPACE
+
+
+def test_rtn_argument_checks_before_any_device_call():
+    lib = G.load()
+    A = 1 << 16
+    W, Q, S_, Z = A, 2 * A, 3 * A, 4 * A
+    call = lambda d_in=64, d_out=8, b=8, w=W, q=Q, s=S_, z=Z: lib.grinqh_quantize_rtn(d_in, d_out, b, w, q, s, z, None)
+    for key in ("w", "q", "s", "z"):
+        assert call(**{key: None}) == B.GRINQH_EINVAL, key
+    assert call(d_in=0) == B.GRINQH_EINVAL
+    assert call(d_out=0) == B.GRINQH_EINVAL
+    assert call(d_out=(1 << 30) + 1) == B.GRINQH_EINVAL
+    for b in (0, 1, 3, 5, 7, 9, 10):
+        assert call(b=b) == B.GRINQH_EINVAL, b
+    assert call(w=W + 1) == B.GRINQH_EALIGN
+    assert call(s=S_ + 1) == B.GRINQH_EALIGN
+    assert call(z=Z + 1) == B.GRINQH_EALIGN
