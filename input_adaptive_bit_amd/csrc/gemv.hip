@@ -141,18 +141,21 @@ struct Batch {
 };
 
 // Issues the plane loads of bucket entries e0, e0 + stride, ... (U of
-// them).  Entries past the bucket end load from past the end of the buffer
-// (zeros, no request).  Lanes whose words lie past the padded row read
-// whatever follows in the buffer: they only feed padded outputs, which are
-// never written and which the epilogue clears.
+// them).  Entries past the bucket end, and lanes whose words lie past the
+// padded row (a tile wider than the layout), load from past the end of the
+// buffer: zeros, no request.  Every other load lies inside its own plane row,
+// so the wave-uniform plane offset never carries an access past the buffer,
+// whether or not the hardware range check counts it.
 struct PlaneSrc {
     __amdgpu_buffer_rsrc_t rsrc;
     uint32_t row_bytes;     // bytes per plane row
-    uint32_t lane_bytes;    // byte offset of this lane's words within a row
+    uint32_t lane_bytes;    // byte offset of this lane's words within a row (kOutOfRange past it)
 };
 
-// Base offset of an entry past the bucket end: the planes are smaller than
-// 2 GiB, so this offset plus any plane offset is past the end of the buffer.
+// Base offset of an entry past the bucket end, and the lane offset of a lane
+// past the row: the planes are smaller than 2 GiB, so this offset plus a
+// channel offset and a plane offset is past the end of the buffer and below
+// 2^32.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 template <int P, int Pb, int V, int U>
@@ -162,7 +165,7 @@ __device__ __forceinline__ void load_batch(Batch<Pb, V, U>& B, const SliceLists&
     for (int u = 0; u < U; ++u) {
         const int e = e0 + u * stride;
         const bool ok = e < end;
-        const uint32_t base = (ok ? L.off[e] : kOutOfRange) + src.lane_bytes;
+        const uint32_t base = ok ? L.off[e] + src.lane_bytes : kOutOfRange;
 #pragma unroll
         for (int p = 0; p < Pb; ++p)
             load_words<V>(src.rsrc, base, static_cast<uint32_t>(p) * src.row_bytes, B.w[u][p]);
@@ -293,7 +296,8 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     // the row size is uniform; make that explicit so plane offsets stay scalar
     src.row_bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(D.row_words) * 4u);
     src.rsrc = planes_rsrc(D.planes, src.row_bytes * static_cast<uint32_t>(P) * static_cast<uint32_t>(D.d_in));
-    src.lane_bytes = static_cast<uint32_t>(word_off) * 4u;
+    // lanes past the row get an offset that keeps every load out of range
+    src.lane_bytes = word_off < D.row_words ? static_cast<uint32_t>(word_off) * 4u : kOutOfRange;
     Bucket<P, 1, V, G> k1;
     Bucket<P, (P >= 2 ? 2 : 1), V, G> k2;
     Bucket<P, (P >= 3 ? 3 : 1), V, G> k3;

@@ -31,6 +31,14 @@ def _theta_dev(theta, dev):
     return to_dev(np.asarray(theta, np.float32), dev)
 
 
+def _mismatch(got, ref, n=8):
+    """The outputs that differ most from the oracle: (index, got, ref)."""
+    got = np.asarray(got, np.float64)
+    d = np.abs(got - ref) / np.maximum(np.abs(ref), 1e-2 * np.sqrt(np.mean(ref ** 2)))
+    idx = np.argsort(-d)[:n]
+    return [(int(j), float(got[j]), float(ref[j])) for j in idx]
+
+
 def _check_y(y_dev, y_ref, tol, what):
     import torch
     y = y_dev.float().cpu().numpy().astype(np.float64)
@@ -178,18 +186,20 @@ def test_gemv_ragged_shapes(dev, b_max, d_in, d_out, x_dtype):
 
 @pytest.mark.parametrize("lane_groups", [1, 2, 4, 8])
 @pytest.mark.parametrize("chunk", [7, 64, 256])
-def test_gemv_forced_launch_shapes(dev, monkeypatch, lane_groups, chunk):
+@pytest.mark.parametrize("b_max", [8, 4])
+def test_gemv_forced_launch_shapes(dev, monkeypatch, lane_groups, chunk, b_max):
     """Every tile width (1, 2, 4 or 8 lane groups per wave) with a short, a
     mid and the longest slice length, forced through the library's tuning
-    overrides, on shapes with several tiles and slices and ragged tails:
-    single calls and a group call against the oracle."""
+    overrides, on shapes with several tiles and slices and ragged tails and on
+    a one-channel layout narrower than one tile: single calls and a group call
+    against the oracle."""
     import torch
     import input_adaptive_bit_amd as G
     monkeypatch.setenv("GRINQH_LANE_GROUPS", str(lane_groups))
     monkeypatch.setenv("GRINQH_CHUNK", str(chunk))
-    rng = np.random.default_rng(lane_groups * 1000 + chunk)
+    rng = np.random.default_rng(lane_groups * 1000 + chunk + b_max)
     members, ops, refs = [], [], []
-    for b_max, (d_in, d_out) in [(8, (1500, 2500)), (8, (513, 4100)), (8, (40, 70))]:
+    for d_in, d_out in [(1500, 2500), (513, 4100), (40, 70), (1, 65)]:
         say(f"forced G={lane_groups} chunk={chunk} b_max={b_max} {d_in}->{d_out}")
         q = rng.integers(0, 1 << b_max, size=(d_out, d_in), dtype=np.uint8)
         s = rng.uniform(0.001, 0.01, d_out).astype(np.float16)
@@ -209,8 +219,9 @@ def test_gemv_forced_launch_shapes(dev, monkeypatch, lane_groups, chunk):
     G.grinqh_gemv_group(layouts, ops, ws)
     torch.cuda.synchronize()
     for k, (o, ref) in enumerate(zip(ops, refs)):
-        err = O.max_rel_error(o[5].cpu().numpy(), ref)
-        assert err <= TOL_F32, (k, err)
+        got = o[5].cpu().numpy()
+        err = O.max_rel_error(got, ref)
+        assert err <= TOL_F32, (k, err, _mismatch(got, ref))
 
 
 def test_gemv_dense_and_all_skipped(dev):
@@ -481,6 +492,9 @@ def test_gemv_group_matches_oracle_and_single_calls(dev, b_max, x_dtype):
         ops.append((xd, td, dl.planes, dl.s, dl.z, y))
         refs.append(C.gemv(x, theta, q, s, z, b_max))
         singles.append(dl.gemv(xd, td, torch.float32))
+    torch.cuda.synchronize()
+    for k, (single, ref) in enumerate(zip(singles, refs)):
+        assert O.max_rel_error(single.cpu().numpy(), ref) <= TOL_F32, ("single", k)
     layouts = [m.L for m in members]
     ws = G.new_group_workspace(layouts, dev)
     for rep in range(3):
@@ -491,5 +505,5 @@ def test_gemv_group_matches_oracle_and_single_calls(dev, b_max, x_dtype):
         for k, (o, ref, single) in enumerate(zip(ops, refs, singles)):
             got = o[5].cpu().numpy()
             err = O.max_rel_error(got, ref)
-            assert err <= TOL_F32, (rep, k, err)
+            assert err <= TOL_F32, (rep, k, err, _mismatch(got, ref))
             assert O.max_rel_error(got, single.cpu().numpy()) <= 5e-4, (rep, k)
