@@ -48,6 +48,11 @@ its reason in the design notes):
   s_j = 0 gets q = 0).  Then s_j * (q + 1/2) + z_j is the midpoint of w's
   interval, within s_j / 2 of w.
 
+* Prefill (the overview: dense b_max weights in the prefill stage, whose
+  19-20% slowdown the page puts down to unpacking).  Every channel is taken at
+  b = b_max whatever its activation: Y = X * W_hat^T with the KD3 weights at
+  k = 0, phi = 1/2.
+
 Parity pins that hold this module to the page and to mathematics are in
 tests/test_oracle_pins.py; none of them retypes the formulas below.
 """
@@ -218,6 +223,25 @@ def gemv_from_planes(x, theta, planes, s, z, b_max: int, d_out: int) -> np.ndarr
 def gemv_columns(x, theta, q_rows, s_cols, z_cols, b_max: int) -> np.ndarray:
     """Outputs for a sample of output channels: q_rows is q[cols, :]."""
     return gemv(x, theta, q_rows, s_cols, z_cols, b_max)
+
+
+# --------------------------------------------------------------------------
+# Prefill stage: the dense b_max dequant GEMM
+# --------------------------------------------------------------------------
+
+def prefill_gemm(X, q, s, z, b_max: int) -> np.ndarray:
+    """Y[m][j] = sum_i X[m][i] * w_hat_ij with every channel at b = b_max, in fp64.
+
+    The page's overview keeps the prefill stage dense: all weights at b_max
+    precision in ordinary matrix products, no thresholds.  With b = b_max for
+    every channel KD3 gives k = 0 and phi = 1/2, so w_hat_ij = s_j * (q_ji +
+    1/2) + z_j on the whole b_max-bit code.  X is [M][d_in] (M prompt tokens),
+    Y is [M][d_out].
+    """
+    X = np.asarray(X, dtype=np.float64)
+    full = np.full(X.shape[-1], b_max, dtype=np.int64)
+    w = dequant(truncated_codes(q, full, b_max), full, s, z, b_max)     # [d_in][d_out]
+    return X @ w
 
 
 # --------------------------------------------------------------------------

@@ -30,6 +30,9 @@ def _pins(golden_dir):
         lambda: pins.test_rtn_codes_at_interval_centres(),
         lambda: pins.test_rtn_round_trip_bound(8),
         lambda: pins.test_rtn_special_rows(),
+        lambda: pins.test_prefill_integer_exact(),
+        lambda: pins.test_prefill_constant_codes_closed_form(),
+        lambda: pins.test_prefill_of_rtn_weights_approximates_the_weights(),
     ]
 
 
@@ -133,7 +136,30 @@ def _mut_rtn_round_not_floor(w, b_max):
     return u.astype(np.uint8), s, z
 
 
+def _mut_prefill_no_midpoint(X, q, s, z, b_max):
+    X = np.asarray(X, np.float64)
+    codes = (np.asarray(q, np.int64) & ((1 << b_max) - 1)).astype(np.float64)
+    return X @ (np.asarray(s, np.float64)[:, None] * codes + np.asarray(z, np.float64)[:, None]).T
+
+
+def _mut_prefill_scale_on_inputs(X, q, s, z, b_max):
+    X = np.asarray(X, np.float64)
+    codes = (np.asarray(q, np.int64) & ((1 << b_max) - 1)).astype(np.float64)
+    s64, z64 = np.asarray(s, np.float64), np.asarray(z, np.float64)
+    s_in = np.resize(s64, codes.shape[1])                 # s read along the input channels
+    return X @ (s_in[None, :] * (codes + 0.5) + z64[:, None]).T
+
+
+def _mut_prefill_top_planes_only(X, q, s, z, b_max):
+    full = np.full(np.asarray(X).shape[-1], max(b_max - 2, 2), dtype=np.int64)
+    w = O.dequant(O.truncated_codes(q, full, b_max), full, s, z, b_max)
+    return np.asarray(X, np.float64) @ w
+
+
 MUTATIONS = {
+    "prefill_without_midpoint": ("prefill_gemm", _mut_prefill_no_midpoint),
+    "prefill_scale_per_input_channel": ("prefill_gemm", _mut_prefill_scale_on_inputs),
+    "prefill_drops_the_last_plane": ("prefill_gemm", _mut_prefill_top_planes_only),
     "rtn_scale_uses_levels_minus_one": ("quantize_rtn", _mut_rtn_scale_minus_one),
     "rtn_rounds_instead_of_floor": ("quantize_rtn", _mut_rtn_round_not_floor),
     "quantile_index_uses_n": ("quantile_position", _mut_quantile_index_n),

@@ -496,3 +496,51 @@ def test_rtn_special_rows():
     assert z[1] == 1.0 and s[1] == np.float16(6.0 / 16) and q[1, 0] == 0
     assert q[1, 7] == 15 and q[1, 1] == 0
     assert np.isinf(s[2]) and np.all(q[2] == 0)
+
+
+# ------------------------------------------------------------- prefill ------
+
+def test_prefill_integer_exact():
+    """s = 1, z = 0 and integer X: 2Y is the exact integer product X (2Q + 1)^T,
+    which fixes the midpoint at b_max and the orientation of Q (non-square)."""
+    rng = np.random.default_rng(21)
+    for b_max in (2, 4, 6, 8):
+        M, d_in, d_out = 5, 7, 11
+        q = rng.integers(0, 256, size=(d_out, d_in))           # high bits are not part of the code
+        X = rng.integers(-9, 10, size=(M, d_in))
+        Y = O.prefill_gemm(X.astype(np.float64), q.astype(np.uint8), np.ones(d_out), np.zeros(d_out), b_max)
+        codes = q & ((1 << b_max) - 1)
+        assert np.array_equal(2 * Y, (X @ (2 * codes + 1).T).astype(np.float64))
+
+
+def test_prefill_constant_codes_closed_form():
+    """q = c, s = sigma, z = zeta everywhere: every weight is sigma (c + 1/2) + zeta,
+    so Y[m][j] is that times the row sum of X."""
+    rng = np.random.default_rng(22)
+    X = rng.normal(size=(4, 33))
+    for b_max, c in ((8, 200), (4, 9), (2, 3), (6, 0)):
+        sigma, zeta = 0.375, -0.0625
+        q = np.full((19, 33), c, np.uint8)
+        Y = O.prefill_gemm(X, q, np.full(19, sigma), np.full(19, zeta), b_max)
+        w = sigma * (c + 0.5) + zeta
+        assert np.allclose(Y, w * X.sum(axis=1)[:, None], rtol=1e-13, atol=1e-13)
+
+
+def test_prefill_of_rtn_weights_approximates_the_weights():
+    """RTN onto the b_max midpoint grid, then the prefill product: each output is
+    within sum_i |X_mi| * (half an interval, plus the fp16 rounding of s and z)
+    of X W^T.  Square and per-output scales, so s or z taken along the wrong
+    axis breaks the bound."""
+    rng = np.random.default_rng(23)
+    n = 96
+    w = rng.normal(0, 0.02, size=(n, n)).astype(np.float32)
+    w *= rng.uniform(0.2, 5.0, size=(n, 1)).astype(np.float32)      # rows of very different range
+    X = rng.normal(size=(6, n))
+    for b_max in (4, 8):
+        q, s, z = O.quantize_rtn(w, b_max)
+        Y = O.prefill_gemm(X, q, s, z, b_max)
+        s64, z64 = s.astype(np.float64), z.astype(np.float64)
+        lo = w.min(axis=1).astype(np.float64)
+        per_w = 0.5 * s64 + np.abs(z64 - lo) + 2.0 ** b_max * np.abs((w.max(axis=1) - lo) / 2.0 ** b_max - s64)
+        bound = np.abs(X) @ np.broadcast_to(per_w, (n, n)) + 1e-12
+        assert np.all(np.abs(Y - X @ w.astype(np.float64).T) <= bound)
