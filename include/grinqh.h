@@ -216,6 +216,32 @@ grinqh_status grinqh_calibrate_thresholds(const void* x, grinqh_dtype x_dtype, i
 grinqh_status grinqh_quantize_rtn(int32_t d_in, int32_t d_out, int32_t b_max, const uint16_t* w,
                                   uint8_t* q, uint16_t* s, uint16_t* z, void* stream);
 
+/* ---- Prefill stage: dense b_max GEMM ----------------------------------
+ *
+ * The note's overview keeps the prefill stage dense: every weight at b_max
+ * precision in ordinary matrix products, no thresholds.  For a block of M
+ * prompt tokens this call computes, with every channel at b = b_max (KD3 at
+ * k = 0, phi = 1/2),
+ *   Y[m][j] = sum_i X[m][i] * (s_j * (q_ji + 1/2) + z_j)
+ * from the same packed planes, s and z as grinqh_gemv.  The products of the
+ * bf16 activations and the integer codes are exact; they are summed in fp32
+ * on the bf16 matrix cores.
+ *   L          layout of the planes (any b_max); d_in must be a multiple of 8.
+ *   x          bf16 [M][d_in], row-major, 16-byte aligned (x_dtype must be
+ *              GRINQH_BF16: the matrix cores take bf16 operands).
+ *   M          1 .. 2^20 tokens.
+ *   planes, s, z  as for grinqh_gemv.
+ *   y          [M][d_out] of y_dtype, row-major, overwritten; bf16 output is
+ *              the fp32 result rounded to nearest even.
+ *   workspace  >= grinqh_prefill_workspace_bytes(M) bytes (the fp32 row sums
+ *              of x), 256-byte aligned, any contents.
+ * x and y must not overlap.  The planes must be smaller than 2 GiB. */
+size_t grinqh_prefill_workspace_bytes(int32_t M);
+grinqh_status grinqh_prefill_gemm(const grinqh_layout* L, const void* x, grinqh_dtype x_dtype, int32_t M,
+                                  const uint32_t* planes, const uint16_t* s, const uint16_t* z, void* y,
+                                  grinqh_dtype y_dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

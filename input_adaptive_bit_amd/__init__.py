@@ -13,4 +13,5 @@ from .grinqh import (  # noqa: F401
     new_workspace, new_group_workspace, pack, assign_bits, gemv, debug_codes,
     grinqh_calibrate_workspace_bytes, grinqh_calibrate_thresholds, calibrate_thresholds,
     grinqh_quantize_rtn, quantize_rtn,
+    grinqh_prefill_workspace_bytes, grinqh_prefill_gemm, prefill_gemm,
 )

@@ -244,6 +244,35 @@ grinqh_status grinqh_gemv_group(const grinqh_layout* layouts, const grinqh_gemv_
                                        static_cast<hipStream_t>(stream)));
 }
 
+size_t grinqh_prefill_workspace_bytes(int32_t M) {
+    return (M < 1 || M > kMaxDim) ? 0 : prefill_workspace_bytes(M);
+}
+
+grinqh_status grinqh_prefill_gemm(const grinqh_layout* L, const void* x, grinqh_dtype x_dtype, int32_t M,
+                                  const uint32_t* planes, const uint16_t* s, const uint16_t* z, void* y,
+                                  grinqh_dtype y_dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    if (!valid_layout(L) || x == nullptr || planes == nullptr || s == nullptr || z == nullptr ||
+        y == nullptr || workspace == nullptr)
+        return GRINQH_EINVAL;
+    if (x_dtype != GRINQH_BF16 || !valid_dtype(y_dtype)) return GRINQH_EINVAL;
+    if (M < 1 || M > kMaxDim || L->d_in % 8 != 0) return GRINQH_EINVAL;
+    if (packed_bytes(L) > kMaxGemvPlaneBytes) return GRINQH_EINVAL;
+    if (prefill_tiles(*L, M) > 0x7FFFFFFFL) return GRINQH_EINVAL;
+    const size_t yb = dtype_bytes(y_dtype);
+    if (!aligned(x, 16) || !aligned(planes, 16) || !aligned(s, 2) || !aligned(z, 2) || !aligned(y, yb) ||
+        !aligned(workspace, 256))
+        return GRINQH_EALIGN;
+    if (workspace_bytes < prefill_workspace_bytes(M)) return GRINQH_ENOSPACE;
+    if (overlap(x, static_cast<size_t>(M) * L->d_in * 2u, y, static_cast<size_t>(M) * L->d_out * yb))
+        return GRINQH_EINVAL;
+    DeviceInfo dev;
+    hipError_t e;
+    if (!current_device_info(&dev, &e)) return map_error(e);
+    return map_error(launch_prefill(*L, static_cast<const uint16_t*>(x), M, planes, s, z, y, y_dtype,
+                                    static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
 grinqh_status grinqh_debug_codes(const grinqh_layout* L, const uint8_t* bits,
                                  const uint32_t* planes, uint8_t* codes, void* stream) {
     if (!valid_layout(L) || bits == nullptr || planes == nullptr || codes == nullptr)

@@ -74,6 +74,13 @@ GemvPlan plan_gemv(const grinqh_layout& L, const LaunchShape& shape);
 // CU count.  GRINQH_LANE_GROUPS and GRINQH_CHUNK override it.
 LaunchShape choose_launch(const grinqh_layout* layouts, int n, const DeviceInfo& dev);
 
+// Prefill GEMM: rows sums, then the MFMA kernel (prefill.hip).
+size_t prefill_workspace_bytes(int M);
+long prefill_tiles(const grinqh_layout& L, int M);
+hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, const uint32_t* planes,
+                          const uint16_t* s, const uint16_t* z, void* y, int y_dtype, float* rowsum,
+                          hipStream_t stream);
+
 void fill_desc(GemvDesc* g, const grinqh_layout& L, const GemvPlan& plan, const void* x, int x_dtype,
                const float* theta, const uint32_t* planes, const uint16_t* s, const uint16_t* z,
                void* y, int y_dtype, void* workspace, int wg_begin);

@@ -46,7 +46,8 @@ MAX_GROUP = 8
 EXPORTS = ("grinqh_version", "grinqh_status_string", "grinqh_layout_init", "grinqh_packed_bytes",
            "grinqh_gemv_workspace_bytes", "grinqh_pack", "grinqh_assign_bits", "grinqh_gemv",
            "grinqh_gemv_group_workspace_bytes", "grinqh_gemv_group", "grinqh_debug_codes",
-           "grinqh_calibrate_workspace_bytes", "grinqh_calibrate_thresholds", "grinqh_quantize_rtn")
+           "grinqh_calibrate_workspace_bytes", "grinqh_calibrate_thresholds", "grinqh_quantize_rtn",
+           "grinqh_prefill_workspace_bytes", "grinqh_prefill_gemm")
 
 _lib = None
 
@@ -99,6 +100,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.grinqh_calibrate_thresholds.restype = ctypes.c_int
     lib.grinqh_quantize_rtn.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
     lib.grinqh_quantize_rtn.restype = ctypes.c_int
+    lib.grinqh_prefill_workspace_bytes.argtypes = [i32]
+    lib.grinqh_prefill_workspace_bytes.restype = sz
+    lib.grinqh_prefill_gemm.argtypes = [LP, vp, ctypes.c_int, i32, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
+    lib.grinqh_prefill_gemm.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -279,6 +284,28 @@ def grinqh_quantize_rtn(w, b_max: int, q, s, z, stream=None) -> None:
            "grinqh_quantize_rtn")
 
 
+def grinqh_prefill_workspace_bytes(M: int) -> int:
+    return int(load().grinqh_prefill_workspace_bytes(int(M)))
+
+
+def grinqh_prefill_gemm(L: Layout, x, planes, s, z, y, workspace, stream=None) -> None:
+    """Prefill-stage dense b_max GEMM: x bf16 [M][d_in] -> y [M][d_out]."""
+    import torch
+    if x.dim() != 2 or y.dim() != 2 or x.shape[1] != L.d_in or y.shape[1] != L.d_out or x.shape[0] != y.shape[0]:
+        raise ValueError("x must be [M][d_in] and y [M][d_out]")
+    M = x.shape[0]
+    _need(x, "x", (torch.bfloat16,), M * L.d_in * 2)
+    _need(planes, "planes", (torch.int32, torch.uint32), grinqh_packed_bytes(L))
+    _need(s, "s", (torch.float16,), 2 * L.d_out)
+    _need(z, "z", (torch.float16,), 2 * L.d_out)
+    _need(y, "y", (torch.bfloat16, torch.float32), M * L.d_out * y.element_size())
+    _need(workspace, "workspace", None)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().grinqh_prefill_gemm(ctypes.byref(L), _ptr(x), _dtype_code(x), M, _ptr(planes), _ptr(s), _ptr(z),
+                                      _ptr(y), _dtype_code(y), _ptr(workspace), ws_bytes, _stream(stream)),
+           "grinqh_prefill_gemm")
+
+
 # ------------------------------------------------- allocating conveniences --
 
 def new_workspace(L: Layout, device=None):
@@ -347,6 +374,18 @@ def quantize_rtn(w, b_max: int, stream=None):
     z = torch.empty(d_out, dtype=torch.float16, device=w.device)
     grinqh_quantize_rtn(w, b_max, q, s, z, stream)
     return q, s, z
+
+
+def prefill_gemm(L: Layout, x, planes, s, z, out_dtype=None, workspace=None, stream=None):
+    """y [M][d_out] of a bf16 token block x [M][d_in] (allocates y and, if not
+    given, the workspace)."""
+    import torch
+    M = x.shape[0]
+    if workspace is None:
+        workspace = torch.empty(max(grinqh_prefill_workspace_bytes(M), 256), dtype=torch.uint8, device=x.device)
+    y = torch.empty((M, L.d_out), dtype=out_dtype or torch.float32, device=x.device)
+    grinqh_prefill_gemm(L, x, planes, s, z, y, workspace, stream)
+    return y
 
 
 def debug_codes(L: Layout, bits, planes, stream=None):

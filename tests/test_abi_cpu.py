@@ -208,3 +208,36 @@ def test_rtn_argument_checks_before_any_device_call():
     assert call(w=W + 1) == B.GRINQH_EALIGN
     assert call(s=S_ + 1) == B.GRINQH_EALIGN
     assert call(z=Z + 1) == B.GRINQH_EALIGN
+
+
+def test_prefill_argument_checks_before_any_device_call():
+    lib = G.load()
+    A = 1 << 20          # 1 MiB-aligned fake addresses, far enough apart for M x d_in
+    L = G.grinqh_layout_init(64, 130, 8)
+    Lp = ctypes.byref(L)
+    X, PL, S, Z, Y, WS = A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A
+    assert lib.grinqh_prefill_workspace_bytes(1) == 256
+    assert lib.grinqh_prefill_workspace_bytes(65) == 512
+    assert lib.grinqh_prefill_workspace_bytes(0) == 0
+
+    def call(L=Lp, x=X, xd=0, M=16, pl=PL, s=S, z=Z, y=Y, yd=1, ws=WS, b=1 << 20):
+        return lib.grinqh_prefill_gemm(L, x, xd, M, pl, s, z, y, yd, ws, b, None)
+
+    for key in ("x", "pl", "s", "z", "y", "ws", "L"):
+        assert call(**{key: None}) == B.GRINQH_EINVAL, key
+    assert call(xd=1) == B.GRINQH_EINVAL                  # the matrix cores take bf16 x
+    assert call(yd=7) == B.GRINQH_EINVAL
+    assert call(M=0) == B.GRINQH_EINVAL
+    assert call(M=(1 << 20) + 1) == B.GRINQH_EINVAL
+    odd = G.grinqh_layout_init(60, 130, 8)                 # d_in not a multiple of 8
+    assert call(L=ctypes.byref(odd)) == B.GRINQH_EINVAL
+    bad = B.Layout(64, 130, 8, 4, 8)                        # row_words inconsistent (12)
+    assert call(L=ctypes.byref(bad)) == B.GRINQH_EINVAL
+    assert call(x=X + 8) == B.GRINQH_EALIGN
+    assert call(pl=PL + 4) == B.GRINQH_EALIGN
+    assert call(y=Y + 2) == B.GRINQH_EALIGN                 # fp32 y
+    assert call(ws=WS + 16) == B.GRINQH_EALIGN
+    assert call(b=255) == B.GRINQH_ENOSPACE
+    assert call(y=X + 64) == B.GRINQH_EINVAL                # y overlaps x
+    big = G.grinqh_layout_init(1 << 20, 4096, 8)           # 4 GiB of planes
+    assert call(L=ctypes.byref(big), M=1, b=1 << 30) == B.GRINQH_EINVAL
