@@ -270,7 +270,7 @@ grinqh_status grinqh_prefill_gemm(const grinqh_layout* L, const void* x, grinqh_
     hipError_t e;
     if (!current_device_info(&dev, &e)) return map_error(e);
     return map_error(launch_prefill(*L, static_cast<const uint16_t*>(x), M, planes, s, z, y, y_dtype,
-                                    static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
+                                    static_cast<float*>(workspace), dev.cu_count, static_cast<hipStream_t>(stream)));
 }
 
 grinqh_status grinqh_debug_codes(const grinqh_layout* L, const uint8_t* bits,

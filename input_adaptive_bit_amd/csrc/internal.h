@@ -74,12 +74,17 @@ GemvPlan plan_gemv(const grinqh_layout& L, const LaunchShape& shape);
 // CU count.  GRINQH_LANE_GROUPS and GRINQH_CHUNK override it.
 LaunchShape choose_launch(const grinqh_layout* layouts, int n, const DeviceInfo& dev);
 
+// Integer value of an environment variable (0 if unset).
+int env_int(const char* name);
+
 // Prefill GEMM: rows sums, then the MFMA kernel (prefill.hip).
 size_t prefill_workspace_bytes(int M);
 long prefill_tiles(const grinqh_layout& L, int M);
+// Tile: 256 x 256 when that alone gives every CU a workgroup, else 128 x 128;
+// GRINQH_PREFILL_TILE (128 or 256) overrides it.
 hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, const uint32_t* planes,
                           const uint16_t* s, const uint16_t* z, void* y, int y_dtype, float* rowsum,
-                          hipStream_t stream);
+                          int cu_count, hipStream_t stream);
 
 void fill_desc(GemvDesc* g, const grinqh_layout& L, const GemvPlan& plan, const void* x, int x_dtype,
                const float* theta, const uint32_t* planes, const uint16_t* s, const uint16_t* z,

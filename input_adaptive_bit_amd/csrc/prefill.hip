@@ -30,10 +30,8 @@
 namespace grinqh {
 namespace {
 
-constexpr int kTM = 128;                 // tokens per workgroup tile
-constexpr int kTN = 128;                 // outputs per workgroup tile
 constexpr int kTK = 64;                  // input channels per stage
-constexpr int kPThreads = 256;           // 4 waves, 2 x 2 quarters of 64 x 64
+constexpr int kPThreads = 256;           // 4 waves, 2 x 2 quarters of the tile
 constexpr uint32_t kPlaneOutOfRange = 0x80000000u;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -55,145 +53,238 @@ __device__ __forceinline__ int tile_off(int r, int c) {
     return r * kTK + ((c ^ (r & 7) ^ ((r >> 4) & 7)) << 3);
 }
 
-// One stage's operands in flight: X chunks of rows (t / 8) + 32 i at chunk
-// t % 8, and the plane words of channels k0 + 2 (t / 8) + {0, 1} at word
-// position n0 / 16 + t % 8.
-template <int P>
+// (channel pair, word position) of plane item i: within every 32 lanes, 8
+// word positions x 4 consecutive pairs, so that the transposing code writes
+// of a half-wave fall on distinct banks and 8 lanes read 32 contiguous bytes
+// of a plane row.
+template <int TN>
+__device__ __forceinline__ int item_word(int i) {
+    if constexpr (TN == 128) return i & 7;
+    else return (i & 7) | (((i >> 5) & 1) << 3);
+}
+template <int TN>
+__device__ __forceinline__ int item_pair(int i) {
+    if constexpr (TN == 128) return i >> 3;
+    else return ((i >> 3) & 3) | ((i >> 6) << 2);
+}
+
+// One stage's operands in flight.  X: chunk item i = t + 256 u is row i / 8,
+// chunk i % 8.  Planes: item i = t + 256 u is the channel pair item_pair(i)
+// at word position item_word(i), both channels' P plane words.
+template <int P, int TM, int TN>
 struct Stage {
-    u32x4 xr[4];
-    uint32_t w[2][P];
+    static constexpr int XI = TM * 8 / kPThreads;          // X chunks per thread
+    static constexpr int WI = (kTK / 2) * (TN / 16) / kPThreads;   // (pair, word) items per thread
+    u32x4 xr[XI];
+    uint32_t w[WI][2][P];
 };
 
-template <int P>
-__device__ __forceinline__ void load_stage(Stage<P>& st, const PrefillArgs& a, int m0, int n0, int k0,
-                                           __amdgpu_buffer_rsrc_t prs, uint32_t row_bytes) {
+template <int P, int TM, int TN>
+__device__ __forceinline__ void load_stage(Stage<P, TM, TN>& st, const PrefillArgs& a, int n0, int k0,
+                                           __amdgpu_buffer_rsrc_t xrs, __amdgpu_buffer_rsrc_t prs,
+                                           uint32_t row_bytes) {
+    using St = Stage<P, TM, TN>;
     const int t = threadIdx.x;
-    const int c = t & 7;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = m0 + (t >> 3) + 32 * i;
-        const int k = k0 + 8 * c;
-        if (m < a.M && k < a.d_in)   // d_in % 8 == 0: a chunk is all in or all out
-            st.xr[i] = *reinterpret_cast<const u32x4*>(a.x + static_cast<size_t>(m) * a.d_in + k);
-        else
-            st.xr[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < St::XI; ++u) {
+        const int i = t + kPThreads * u;
+        const int k = k0 + 8 * (i & 7);
+        // rows past M lie past the resource; d_in % 8 == 0, so a chunk is
+        // all in or all out of the row
+        const uint32_t off = k < a.d_in ? static_cast<uint32_t>((i >> 3) * a.d_in + k) * 2u : kPlaneOutOfRange;
+        st.xr[u] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
     }
-    const int word = (n0 >> 4) + (t & 7);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int ch = k0 + 2 * (t >> 3) + h;
-        const bool ok = ch < a.d_in && word < a.row_words;
-        // inside channel ch's P plane rows, so a plane offset keeps it in the buffer
-        const uint32_t off = ok ? (static_cast<uint32_t>(ch) * P * static_cast<uint32_t>(a.row_words) +
-                                   static_cast<uint32_t>(word)) * 4u
-                                : kPlaneOutOfRange;
+    for (int u = 0; u < St::WI; ++u) {
+        const int i = t + kPThreads * u;
+        const int word = (n0 >> 4) + item_word<TN>(i);
 #pragma unroll
-        for (int p = 0; p < P; ++p)
-            st.w[h][p] = __builtin_amdgcn_raw_buffer_load_b32(prs, off, static_cast<uint32_t>(p) * row_bytes, 0);
+        for (int h = 0; h < 2; ++h) {
+            const int ch = k0 + 2 * item_pair<TN>(i) + h;
+            const bool ok = ch < a.d_in && word < a.row_words;
+            // inside channel ch's P plane rows, so a plane offset keeps it in the buffer
+            const uint32_t off = ok ? (static_cast<uint32_t>(ch) * P * static_cast<uint32_t>(a.row_words) +
+                                       static_cast<uint32_t>(word)) * 4u
+                                    : kPlaneOutOfRange;
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                st.w[u][h][p] = __builtin_amdgcn_raw_buffer_load_b32(prs, off, static_cast<uint32_t>(p) * row_bytes, 0);
+        }
     }
+}
+
+// Decoded plane words of a prefetched stage: per item and channel, the four
+// merge_codes words (byte b of word k: the code of output 4b + k, scaled by
+// the byte lane's constant, undone in the epilogue).
+template <int P, int TM, int TN>
+struct Merged {
+    uint32_t E[Stage<P, TM, TN>::WI][2][4];
+};
+
+template <int P, int TM, int TN>
+__device__ __forceinline__ void merge_stage(const Stage<P, TM, TN>& st, Merged<P, TM, TN>& mg) {
+#pragma unroll
+    for (int u = 0; u < Stage<P, TM, TN>::WI; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            merge_codes<P>(st.w[u][h], mg.E[u][h]);
+            // hide the known-zero bits so that each byte becomes one
+            // v_cvt_f32_ubyte (this also ends the scheduling region, so the
+            // merges stay ahead of the matrix work)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) asm("" : "+v"(mg.E[u][h][k]));
+        }
 }
 
 // Writes a prefetched stage into one LDS buffer: X chunks as they are, and
-// the codes of both channels as bf16 pairs (channel 2 (t / 8) in the low
-// half) at every output of the word position.  Code bytes carry the scale
-// merge_codes leaves in byte lane k, undone in the epilogue.
-template <int P>
-__device__ __forceinline__ void store_stage(const Stage<P>& st, uint16_t* xs, uint16_t* ws) {
+// the codes of both channels of a pair as bf16 pairs (the even channel in
+// the low half) at every output of the word position.
+template <int P, int TM, int TN>
+__device__ __forceinline__ void store_stage(const Stage<P, TM, TN>& st, const Merged<P, TM, TN>& mg, uint16_t* xs,
+                                            uint16_t* ws) {
+    using St = Stage<P, TM, TN>;
     const int t = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(xs + tile_off((t >> 3) + 32 * i, t & 7)) = st.xr[i];
-    uint32_t E0[4], E1[4];
-    merge_codes<P>(st.w[0], E0);
-    merge_codes<P>(st.w[1], E1);
-    // hide the known-zero bits so that each byte becomes one v_cvt_f32_ubyte
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        asm("" : "+v"(E0[k]));
-        asm("" : "+v"(E1[k]));
+    for (int u = 0; u < St::XI; ++u) {
+        const int i = t + kPThreads * u;
+        *reinterpret_cast<u32x4*>(xs + tile_off(i >> 3, i & 7)) = st.xr[u];
     }
-    const int cp = t >> 3;
-    const int chunk = cp >> 2;
-    const int elem = (2 * cp) & 7;
-    const int row0 = 16 * (t & 7);
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int u = 0; u < St::WI; ++u) {
+        const int i = t + kPThreads * u;
+        const int cp = item_pair<TN>(i);
+        const int chunk = cp >> 2;
+        const int elem = (2 * cp) & 7;
+        const int row0 = 16 * item_word<TN>(i);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const float v0 = byte_f32(E0[k], b), v1 = byte_f32(E1[k], b);
-            // integers <= 255: the bf16 is the upper half of the fp32, exactly
-            const uint32_t pair = __builtin_amdgcn_perm(__float_as_uint(v1), __float_as_uint(v0), 0x07060302u);
-            *reinterpret_cast<uint32_t*>(ws + tile_off(row0 + 4 * b + k, chunk) + elem) = pair;
-        }
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float v0 = byte_f32(mg.E[u][0][k], b), v1 = byte_f32(mg.E[u][1][k], b);
+                // integers <= 255: the bf16 is the upper half of the fp32, exactly
+                const uint32_t pair = __builtin_amdgcn_perm(__float_as_uint(v1), __float_as_uint(v0), 0x07060302u);
+                *reinterpret_cast<uint32_t*>(ws + tile_off(row0 + 4 * b + k, chunk) + elem) = pair;
+            }
+    }
 }
 
-__device__ __forceinline__ void mma_stage(f32x16 (&acc)[2][2], const uint16_t* xs, const uint16_t* ws, int wm,
-                                          int wn, int lane) {
+// One wave's (TM / 2) x (TN / 2) quarter: FM x FN tiles of 32 x 32.
+template <int FM, int FN>
+__device__ __forceinline__ void mma_stage(f32x16 (&acc)[FM][FN], const uint16_t* xs, const uint16_t* ws,
+                                          int row_a, int row_b, int lane) {
 #pragma unroll
     for (int kk = 0; kk < kTK / 16; ++kk) {
         const int c = 2 * kk + (lane >> 5);
-        bf16x8 av[2], bv[2];
+        bf16x8 av[FM], bv[FN];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            av[i] = *reinterpret_cast<const bf16x8*>(xs + tile_off(64 * wm + 32 * i + (lane & 31), c));
-            bv[i] = *reinterpret_cast<const bf16x8*>(ws + tile_off(64 * wn + 32 * i + (lane & 31), c));
-        }
+        for (int i = 0; i < FM; ++i)
+            av[i] = *reinterpret_cast<const bf16x8*>(xs + tile_off(row_a + 32 * i + (lane & 31), c));
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < FN; ++j)
+            bv[j] = *reinterpret_cast<const bf16x8*>(ws + tile_off(row_b + 32 * j + (lane & 31), c));
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
 }
 
-template <int P>
-__global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kTM * kTK];
-    __shared__ __attribute__((aligned(16))) uint16_t wsh[2][kTN * kTK];
-    __shared__ float srow[kTM];
+// Scheduling hint for one loop body: the stage's loads first, then every
+// MFMA followed by a share of the decode VALU work, an LDS write and, for
+// every other MFMA, an operand read, so that the decode of the next stage
+// runs while the matrix cores work on this one.
+template <int I, int N, int R, int V, int W>
+__device__ __forceinline__ void interleave_step() {
+    if constexpr (I < N) {
+        if constexpr (I * R / N != (I + 1) * R / N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                          // MFMA
+        constexpr int v = (I + 1) * V / N - I * V / N;
+        if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x002, v, 0);                    // VALU
+        constexpr int w = (I + 1) * W / N - I * W / N;
+        if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);                    // DS write
+        interleave_step<I + 1, N, R, V, W>();
+    }
+}
+
+template <int P, int TM, int TN>
+__device__ __forceinline__ void interleave() {
+    using St = Stage<P, TM, TN>;
+    constexpr int kMfma = (TM / 64) * (TN / 64) * (kTK / 16);
+    constexpr int kReads = (TM / 64 + TN / 64) * (kTK / 16);
+    constexpr int kWrites = St::XI + St::WI * 16;
+    constexpr int kValu = St::WI * 16 * 3;
+    interleave_step<0, kMfma, kReads, kValu, kWrites>();
+}
+
+template <int P, int TM, int TN>
+__global__ __launch_bounds__(kPThreads, (TM * TN > 128 * 128 ? 1 : 2)) void prefill_kernel(PrefillArgs a) {
+    constexpr int FM = TM / 64, FN = TN / 64;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][TM * kTK];
+    __shared__ __attribute__((aligned(16))) uint16_t wsh[2][TN * kTK];
+    __shared__ float srow[TM];
     const int id = static_cast<int>(blockIdx.x);
-    const int m0 = (id % a.tiles_m) * kTM;
-    const int n0 = (id / a.tiles_m) * kTN;
+    const int m0 = (id % a.tiles_m) * TM;
+    const int n0 = (id / a.tiles_m) * TN;
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
-    const int wm = wv >> 1, wn = wv & 1;
+    const int row_a = (wv >> 1) * (TM / 2);     // this wave's first token row in the tile
+    const int row_b = (wv & 1) * (TN / 2);      // and first output
     const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint32_t*>(a.planes), static_cast<short>(0), static_cast<int>(a.plane_bytes), 0x00020000);
     const uint32_t row_bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a.row_words) * 4u);
+    const int rows = min(TM, a.M - m0);
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.x + static_cast<size_t>(m0) * a.d_in), static_cast<short>(0),
+        rows * a.d_in * 2, 0x00020000);
 
-    f32x16 acc[2][2];
+    f32x16 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int n_stages = (a.d_in + kTK - 1) / kTK;
-    Stage<P> st;
-    load_stage<P>(st, a, m0, n0, 0, prs, row_bytes);
-    store_stage<P>(st, xs[0], wsh[0]);
+    // Stage s is computed from LDS while stage s + 1, loaded one iteration
+    // earlier, is decoded into the other LDS buffer and stage s + 2 is
+    // loaded; stages past the last load nothing (out-of-range offsets).
+    Stage<P, TM, TN> sa, sb;
+    Merged<P, TM, TN> mg;
+    load_stage<P, TM, TN>(sa, a, n0, 0, xrs, prs, row_bytes);
+    merge_stage<P, TM, TN>(sa, mg);
+    store_stage<P, TM, TN>(sa, mg, xs[0], wsh[0]);
+    load_stage<P, TM, TN>(sa, a, n0, kTK, xrs, prs, row_bytes);
     __syncthreads();
-    for (int s = 0; s < n_stages; ++s) {
-        const int cur = s & 1;
-        const bool more = s + 1 < n_stages;
-        if (more) load_stage<P>(st, a, m0, n0, (s + 1) * kTK, prs, row_bytes);
-        mma_stage(acc, xs[cur], wsh[cur], wm, wn, lane);
-        if (more) store_stage<P>(st, xs[cur ^ 1], wsh[cur ^ 1]);
+    int s = 0;
+    for (; s + 1 < n_stages; s += 2) {
+        load_stage<P, TM, TN>(sb, a, n0, (s + 2) * kTK, xrs, prs, row_bytes);
+        merge_stage<P, TM, TN>(sa, mg);
+        mma_stage<FM, FN>(acc, xs[0], wsh[0], row_a, row_b, lane);
+        store_stage<P, TM, TN>(sa, mg, xs[1], wsh[1]);
+        interleave<P, TM, TN>();
+        __syncthreads();
+        load_stage<P, TM, TN>(sa, a, n0, (s + 3) * kTK, xrs, prs, row_bytes);
+        merge_stage<P, TM, TN>(sb, mg);
+        mma_stage<FM, FN>(acc, xs[1], wsh[1], row_a, row_b, lane);
+        store_stage<P, TM, TN>(sb, mg, xs[0], wsh[0]);
+        interleave<P, TM, TN>();
         __syncthreads();
     }
+    if (s < n_stages) mma_stage<FM, FN>(acc, xs[0], wsh[0], row_a, row_b, lane);
 
-    if (threadIdx.x < kTM) {
-        const int m = m0 + static_cast<int>(threadIdx.x);
-        srow[threadIdx.x] = m < a.M ? a.rowsum[m] : 0.f;
+    for (int r = threadIdx.x; r < TM; r += kPThreads) {
+        const int m = m0 + r;
+        srow[r] = m < a.M ? a.rowsum[m] : 0.f;
     }
     __syncthreads();
 
     // y = s_j * u_j * acc + (s_j / 2 + z_j) * S_m, u_j undoing the byte scale
     // of output j's lane in merge_codes (outputs 4b + k sit in byte lane k)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int n = n0 + 64 * wn + 32 * j + (lane & 31);
+    for (int j = 0; j < FN; ++j) {
+        const int n = n0 + row_b + 32 * j + (lane & 31);
         const bool n_ok = n < a.d_out;
         const int nc = n_ok ? n : a.d_out - 1;
         const float sj = f16_to_f32(a.s[nc]);
@@ -201,10 +292,10 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_kernel(PrefillArgs a) {
         const float mul = sj * code_unscale<P>(lane & 3);
         const float add = 0.5f * sj + zj;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int ml = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int ml = row_a + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 const int m = m0 + ml;
                 if (!n_ok || m >= a.M) continue;
                 const float yv = mul * acc[i][j][r] + add * srow[ml];
@@ -239,10 +330,21 @@ __global__ __launch_bounds__(256) void rowsum_kernel(const uint16_t* x, int d_in
     if (threadIdx.x == 0) out[blockIdx.x] = red[0];
 }
 
-template <int P>
-hipError_t launch_p(const PrefillArgs& a, int tiles, hipStream_t stream) {
-    prefill_kernel<P><<<dim3(static_cast<unsigned>(tiles)), dim3(kPThreads), 0, stream>>>(a);
+template <int P, int TM, int TN>
+hipError_t launch_t(PrefillArgs a, hipStream_t stream) {
+    a.tiles_m = (a.M + TM - 1) / TM;
+    const long tiles = static_cast<long>(a.tiles_m) * ((a.d_out + TN - 1) / TN);
+    prefill_kernel<P, TM, TN><<<dim3(static_cast<unsigned>(tiles)), dim3(kPThreads), 0, stream>>>(a);
     return hipGetLastError();
+}
+
+template <int P>
+hipError_t launch_p(const PrefillArgs& a, bool big, hipStream_t stream) {
+    return big ? launch_t<P, 256, 256>(a, stream) : launch_t<P, 128, 128>(a, stream);
+}
+
+long tiles_of(int M, int d_out, int tm, int tn) {
+    return static_cast<long>((M + tm - 1) / tm) * ((d_out + tn - 1) / tn);
 }
 
 }  // namespace
@@ -251,13 +353,13 @@ size_t prefill_workspace_bytes(int M) {
     return M <= 0 ? 0 : (static_cast<size_t>(M) * sizeof(float) + 255) / 256 * 256;
 }
 
-long prefill_tiles(const grinqh_layout& L, int M) {
-    return static_cast<long>((M + kTM - 1) / kTM) * ((L.d_out + kTN - 1) / kTN);
-}
+long prefill_tiles(const grinqh_layout& L, int M) { return tiles_of(M, L.d_out, 128, 128); }
 
+// 256 x 256 tiles (one workgroup per CU) once they alone give every CU a
+// workgroup; 128 x 128 tiles (two per CU) for smaller products.
 hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, const uint32_t* planes,
                           const uint16_t* s, const uint16_t* z, void* y, int y_dtype, float* rowsum,
-                          hipStream_t stream) {
+                          int cu_count, hipStream_t stream) {
     rowsum_kernel<<<dim3(static_cast<unsigned>(M)), dim3(256), 0, stream>>>(x, L.d_in, rowsum);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -273,14 +375,15 @@ hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, cons
     a.d_out = L.d_out;
     a.row_words = L.row_words;
     a.y_dtype = y_dtype;
-    a.tiles_m = (M + kTM - 1) / kTM;
     a.plane_bytes = static_cast<uint32_t>(static_cast<size_t>(L.d_in) * L.n_planes * L.row_words * 4u);
-    const int tiles = static_cast<int>(prefill_tiles(L, M));
+    bool big = tiles_of(M, L.d_out, 256, 256) >= cu_count;
+    const int env = env_int("GRINQH_PREFILL_TILE");
+    if (env == 128 || env == 256) big = env == 256;
     switch (L.n_planes) {
-        case 1: return launch_p<1>(a, tiles, stream);
-        case 2: return launch_p<2>(a, tiles, stream);
-        case 3: return launch_p<3>(a, tiles, stream);
-        case 4: return launch_p<4>(a, tiles, stream);
+        case 1: return launch_p<1>(a, big, stream);
+        case 2: return launch_p<2>(a, big, stream);
+        case 3: return launch_p<3>(a, big, stream);
+        case 4: return launch_p<4>(a, big, stream);
         default: return hipErrorInvalidValue;
     }
 }

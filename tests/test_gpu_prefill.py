@@ -182,3 +182,23 @@ def test_prefill_full_size_sampled(dev, b_max):
     err = _row_err(Y, R)
     say(f"  sampled rows: max rel err {err:.3e}")
     assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("b_max", [2, 8])
+def test_prefill_forced_tiles(dev, monkeypatch, tile, b_max):
+    """Both tile sizes, forced through the library's override, on shapes with
+    ragged token, channel and output tails."""
+    import torch
+    import input_adaptive_bit_amd as G
+    monkeypatch.setenv("GRINQH_PREFILL_TILE", str(tile))
+    for M, d_in, d_out in [(300, 4104, 700), (5, 64, 130), (257, 136, 513), (512, 512, 512)]:
+        say(f"prefill forced tile {tile} b_max={b_max} M={M} {d_in}->{d_out}")
+        rng = np.random.default_rng(tile + b_max + M + d_in + d_out)
+        q, s, z, X = _inputs(rng, M, d_in, d_out, b_max)
+        dl = DeviceLinear(q, s, z, b_max, dev)
+        xd, Xh = _x_dev(X, dev)
+        y = G.prefill_gemm(dl.L, xd, dl.planes, dl.s, dl.z, torch.float32)
+        torch.cuda.synchronize()
+        err = _row_err(y.cpu().numpy().astype(np.float64), O.prefill_gemm(Xh, q, s, z, b_max))
+        assert err <= TOL_F32, (M, d_in, d_out, err)
