@@ -190,31 +190,77 @@ __device__ __forceinline__ void mma_stage(f32x16 (&acc)[FM][FN], const uint16_t*
     }
 }
 
-// Scheduling hint for one loop body: the stage's loads first, then every
-// MFMA followed by a share of the decode VALU work, an LDS write and, for
-// every other MFMA, an operand read, so that the decode of the next stage
-// runs while the matrix cores work on this one.
-template <int I, int N, int R, int V, int W>
-__device__ __forceinline__ void interleave_step() {
-    if constexpr (I < N) {
-        if constexpr (I * R / N != (I + 1) * R / N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                          // MFMA
-        constexpr int v = (I + 1) * V / N - I * V / N;
-        if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x002, v, 0);                    // VALU
-        constexpr int w = (I + 1) * W / N - I * W / N;
-        if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);                    // DS write
-        interleave_step<I + 1, N, R, V, W>();
+// One k-step's MFMA operands of a wave: FM row fragments of X and FN of the
+// codes, 8 consecutive channels per lane.
+template <int FM, int FN>
+struct Frag {
+    bf16x8 a[FM], b[FN];
+};
+
+template <int FM, int FN>
+__device__ __forceinline__ void read_frags(Frag<FM, FN>& f, const uint16_t* xs, const uint16_t* ws, int kk,
+                                           int row_a, int row_b, int lane) {
+    const int c = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+        f.a[i] = *reinterpret_cast<const bf16x8*>(xs + tile_off(row_a + 32 * i + (lane & 31), c));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+        f.b[j] = *reinterpret_cast<const bf16x8*>(ws + tile_off(row_b + 32 * j + (lane & 31), c));
+}
+
+// Decode unit U of the next stage: output 4b + k of item u's word position,
+// both channels of the pair, one bf16 pair into the LDS code tile.
+template <int P, int TM, int TN, int U>
+__device__ __forceinline__ void code_unit(const Merged<P, TM, TN>& mg, uint16_t* ws) {
+    constexpr int u = U / 16, k = (U % 16) / 4, b = U % 4;
+    const int i = static_cast<int>(threadIdx.x) + kPThreads * u;
+    const int cp = item_pair<TN>(i);
+    const float v0 = byte_f32(mg.E[u][0][k], b), v1 = byte_f32(mg.E[u][1][k], b);
+    // integers <= 255: the bf16 is the upper half of the fp32, exactly
+    const uint32_t pair = __builtin_amdgcn_perm(__float_as_uint(v1), __float_as_uint(v0), 0x07060302u);
+    *reinterpret_cast<uint32_t*>(ws + tile_off(16 * item_word<TN>(i) + 4 * b + k, cp >> 2) + ((2 * cp) & 7)) = pair;
+}
+
+template <int P, int TM, int TN, int U0, int U1>
+__device__ __forceinline__ void code_units(const Merged<P, TM, TN>& mg, uint16_t* ws) {
+    if constexpr (U0 < U1) {
+        code_unit<P, TM, TN, U0>(mg, ws);
+        code_units<P, TM, TN, U0 + 1, U1>(mg, ws);
     }
 }
 
-template <int P, int TM, int TN>
-__device__ __forceinline__ void interleave() {
-    using St = Stage<P, TM, TN>;
-    constexpr int kMfma = (TM / 64) * (TN / 64) * (kTK / 16);
-    constexpr int kReads = (TM / 64 + TN / 64) * (kTK / 16);
-    constexpr int kWrites = St::XI + St::WI * 16;
-    constexpr int kValu = St::WI * 16 * 3;
-    interleave_step<0, kMfma, kReads, kValu, kWrites>();
+template <int P, int TM, int TN, int X0, int X1>
+__device__ __forceinline__ void x_units(const Stage<P, TM, TN>& st, uint16_t* xs) {
+    if constexpr (X0 < X1) {
+        const int i = static_cast<int>(threadIdx.x) + kPThreads * X0;
+        *reinterpret_cast<u32x4*>(xs + tile_off(i >> 3, i & 7)) = st.xr[X0];
+        x_units<P, TM, TN, X0 + 1, X1>(st, xs);
+    }
+}
+
+// MFMA G of a stage (k-step G / (FM FN)), followed by its share of the next
+// stage's decode and X writes, in a fixed order (scheduling fences), so that
+// the decode runs on the vector units while the matrix cores work.  Halfway
+// through a k-step the next k-step's operands are read into the other
+// fragment set.
+template <int G, int P, int TM, int TN>
+__device__ __forceinline__ void step(f32x16 (&acc)[TM / 64][TN / 64], Frag<TM / 64, TN / 64> (&fr)[2],
+                                     const uint16_t* xs, const uint16_t* ws, const Stage<P, TM, TN>& st,
+                                     const Merged<P, TM, TN>& mg, uint16_t* xs_next, uint16_t* ws_next,
+                                     int row_a, int row_b, int lane) {
+    constexpr int FM = TM / 64, FN = TN / 64, PER = FM * FN, NM = PER * (kTK / 16);
+    if constexpr (G < NM) {
+        constexpr int kk = G / PER, mi = G % PER, i = mi / FN, j = mi % FN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kk & 1].a[i], fr[kk & 1].b[j], acc[i][j], 0, 0, 0);
+        if constexpr (mi == PER / 2 && kk + 1 < kTK / 16)
+            read_frags<FM, FN>(fr[(kk + 1) & 1], xs, ws, kk + 1, row_a, row_b, lane);
+        constexpr int NU = Stage<P, TM, TN>::WI * 16, XI = Stage<P, TM, TN>::XI;
+        code_units<P, TM, TN, G * NU / NM, (G + 1) * NU / NM>(mg, ws_next);
+        x_units<P, TM, TN, G * XI / NM, (G + 1) * XI / NM>(st, xs_next);
+        __builtin_amdgcn_sched_barrier(0);
+        step<G + 1, P, TM, TN>(acc, fr, xs, ws, st, mg, xs_next, ws_next, row_a, row_b, lane);
+    }
 }
 
 template <int P, int TM, int TN>
@@ -252,6 +298,7 @@ __global__ __launch_bounds__(kPThreads, (TM * TN > 128 * 128 ? 1 : 2)) void pref
     // loaded; stages past the last load nothing (out-of-range offsets).
     Stage<P, TM, TN> sa, sb;
     Merged<P, TM, TN> mg;
+    Frag<FM, FN> fr[2];
     load_stage<P, TM, TN>(sa, a, n0, 0, xrs, prs, row_bytes);
     merge_stage<P, TM, TN>(sa, mg);
     store_stage<P, TM, TN>(sa, mg, xs[0], wsh[0]);
@@ -261,15 +308,13 @@ __global__ __launch_bounds__(kPThreads, (TM * TN > 128 * 128 ? 1 : 2)) void pref
     for (; s + 1 < n_stages; s += 2) {
         load_stage<P, TM, TN>(sb, a, n0, (s + 2) * kTK, xrs, prs, row_bytes);
         merge_stage<P, TM, TN>(sa, mg);
-        mma_stage<FM, FN>(acc, xs[0], wsh[0], row_a, row_b, lane);
-        store_stage<P, TM, TN>(sa, mg, xs[1], wsh[1]);
-        interleave<P, TM, TN>();
+        read_frags<FM, FN>(fr[0], xs[0], wsh[0], 0, row_a, row_b, lane);
+        step<0, P, TM, TN>(acc, fr, xs[0], wsh[0], sa, mg, xs[1], wsh[1], row_a, row_b, lane);
         __syncthreads();
         load_stage<P, TM, TN>(sa, a, n0, (s + 3) * kTK, xrs, prs, row_bytes);
         merge_stage<P, TM, TN>(sb, mg);
-        mma_stage<FM, FN>(acc, xs[1], wsh[1], row_a, row_b, lane);
-        store_stage<P, TM, TN>(sb, mg, xs[0], wsh[0]);
-        interleave<P, TM, TN>();
+        read_frags<FM, FN>(fr[0], xs[1], wsh[1], 0, row_a, row_b, lane);
+        step<0, P, TM, TN>(acc, fr, xs[1], wsh[1], sb, mg, xs[0], wsh[0], row_a, row_b, lane);
         __syncthreads();
     }
     if (s < n_stages) mma_stage<FM, FN>(acc, xs[0], wsh[0], row_a, row_b, lane);
