@@ -18,8 +18,12 @@ stored at b_max 6 (levels 0/2/4/6) at 2/3/4/6 effective bits, the whole
 32-layer decode step (128 launches in dependency order: per layer the fused
 q|k|v, o, fused gate|up and down projections; 7.0 GB of planes at b_max 8) at
 the same effective bits, the offline threshold calibration (exact quantiles of
-128 samples' |x|) and RTN quantisation (bf16 weights to b_max 8 codes), and the
-plain fp64 C oracle timed on the host cores over a bounded sample.
+128 samples' |x|) and RTN quantisation (bf16 weights to b_max 8 codes), the
+prefill-stage dense b_max GEMM on the matrix cores (2048 tokens through a
+4096->16384 up projection at b_max 8 and 4, and through 4096->4096; TFLOP/s
+against the bf16 matrix peak, with torch's bf16 matmul of a dense weight of the
+same shape beside it), and the plain fp64 C oracle timed on the host cores over
+a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -40,6 +44,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "GEMV µs and required-bytes HBM GB/s (% of MI355X peak) at 2/3/4/8 eff. bits"
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
@@ -238,6 +243,7 @@ def main() -> int:
     ap.add_argument("--no-b6", action="store_true", help="skip the b_max 6 sweep")
     ap.add_argument("--no-decode-step", action="store_true",
                     help="skip the 32-layer decode-step measurement (7.0 GB of planes)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-stage GEMM timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copies", type=int, default=0, help="weight copies (0: enough for 512 MB)")
@@ -409,6 +415,49 @@ def main() -> int:
             del g, wt, qt
             log(f"rtn {di}x{do}: {t:.1f} us, {moved / t / 1e3:.1f} GB/s")
 
+    prefill = {}
+    if not args.no_prefill:
+        # prefill stage: a block of prompt tokens through dense b_max weights
+        for (M, di, do), bm in (((2048, 4096, 16384), 8), ((2048, 4096, 16384), 4), ((2048, 4096, 4096), 8)):
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(S.torch_seed((2, 10, di, do), bm))
+            qd = torch.randint(0, 1 << bm, (do, di), dtype=torch.uint8, device=dev, generator=gen)
+            Lp, pl = G.pack(qd, bm)
+            sp = (torch.rand(do, generator=gen, device=dev) * 0.009 + 0.001).half()
+            zp = (torch.randn(do, generator=gen, device=dev) * 0.01).half()
+            xp = torch.randn((M, di), generator=gen, device=dev).to(torch.bfloat16)
+            yp = torch.empty((M, do), dtype=torch.bfloat16, device=dev)
+            wsp = torch.empty(G.grinqh_prefill_workspace_bytes(M), dtype=torch.uint8, device=dev)
+
+            def pre(reps=4):
+                for _ in range(reps):
+                    G.grinqh_prefill_gemm(Lp, xp, pl, sp, zp, yp, wsp)
+            g = capture(pre)
+            time_graph(g)
+            t = time_graph(g) * 1e3 / 4
+            flops = 2.0 * M * di * do
+            # the same product on a dense bf16 weight through torch (hipBLASLt), for context
+            wd = torch.randn((do, di), generator=gen, device=dev).to(torch.bfloat16)
+            for _ in range(3):
+                torch.matmul(xp, wd.t())
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                torch.matmul(xp, wd.t())
+            e1.record()
+            torch.cuda.synchronize()
+            tt = e0.elapsed_time(e1) * 1e3 / 10
+            prefill[f"{M}x{di}->{do} b_max {bm}"] = {
+                "us": round(t, 2), "TFLOP/s": round(flops / t / 1e6, 1),
+                "frac_of_bf16_mfma_peak": round(flops / t / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "tokens_per_s": round(M / t * 1e6), "torch_bf16_dense_us": round(tt, 2),
+                "torch_bf16_dense_TFLOP/s": round(flops / tt / 1e6, 1), "vs_torch_dense": round(tt / t, 3)}
+            del g, qd, pl, xp, yp, wd
+            torch.cuda.empty_cache()
+            log(f"prefill {M}x{di}->{do} b_max {bm}: {t:.1f} us, {flops / t / 1e6:.1f} TFLOP/s; "
+                f"torch bf16 dense {tt:.1f} us")
+
     decode_step = {}
     if not args.no_decode_step:
         del step
@@ -477,6 +526,7 @@ def main() -> int:
         "threshold_calibration": calibration,
         "rtn_quantisation_b_max_8": rtn,
         "decode_step_32_layers": decode_step,
+        "prefill_gemm": prefill,
     }
     print(json.dumps(out), flush=True)
     return 0

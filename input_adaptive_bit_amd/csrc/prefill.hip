@@ -10,19 +10,22 @@
 // (q <= 255, exact in bf16), so it runs on the bf16 matrix cores with fp32
 // accumulation (v_mfma_f32_32x32x16_bf16); S comes from a row-sum pass.
 //
-// Tiling.  A workgroup computes a 128-token x 128-output tile of Y and walks
-// the input channels in stages of 64.  Its four waves own 64 x 64 quarters,
-// each four 32 x 32 MFMA tiles.  Per stage every thread prefetches into
-// registers four 16-byte chunks of X and, for two adjacent channels, the P
-// plane words of one 16-output word position; while the matrix cores work on
-// the current stage it decodes the prefetched words (merge_codes, shared with
-// the decode GEMV) into bf16 channel pairs and writes both operands into the
-// other half of a double-buffered LDS tile.
+// Tiling.  A workgroup computes a T x T tile of Y (T = 256, one workgroup per
+// CU, accumulators in AGPRs; or T = 128, two per CU) and walks the input
+// channels in stages of 64.  Its four waves own (T/2) x (T/2) quarters of
+// 32 x 32 MFMA tiles.  Every thread holds, two stages ahead, 16-byte chunks
+// of X and the P plane words of a channel pair at one 16-output word
+// position.  While the matrix cores work on stage s, the waves decode stage
+// s + 1 (merge_codes, shared with the decode GEMV, then one byte conversion
+// per code and one permute per bf16 channel pair) into the other half of a
+// double-buffered LDS tile: each MFMA is followed, in a fixed order, by its
+// share of that work.
 //
-// LDS tiles are [128 rows][64 channels] of bf16, rows of 8 16-byte chunks,
+// LDS tiles are [T rows][64 channels] of bf16, rows of 8 16-byte chunks,
 // with chunk c of row r stored at chunk c ^ (r & 7) ^ ((r >> 4) & 7): the
 // MFMA operand reads (8 consecutive rows, one chunk) and the transposing
-// code writes (rows 16 apart, one chunk pair) both spread over all banks.
+// code writes (one row per word position, a chunk of four channel pairs)
+// both spread over all banks.
 #include "decode.hpp"
 #include "device_common.hpp"
 #include "internal.h"
