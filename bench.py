@@ -210,7 +210,7 @@ def time_graph(g, reps: int = 1) -> float:
     return st.elapsed_time(en)
 
 
-def cpu_baseline(shapes, eff, seconds: float):
+def cpu_baseline(shapes, eff, seconds: float, prefill: bool = True):
     from oracle import c_oracle
     per_step = sum(sh.req[eff] for sh in shapes)
     t0 = time.perf_counter()
@@ -222,7 +222,7 @@ def cpu_baseline(shapes, eff, seconds: float):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {
+    out = {
         "value": round(per_step * passes / el / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
@@ -230,6 +230,24 @@ def cpu_baseline(shapes, eff, seconds: float):
         "sample": (f"{passes} full passes of the 3 linears at ~{eff} eff. bits "
                    f"(plain fp64 C oracle, one thread, {el:.1f} s)"),
     }
+    if prefill:
+        # the prefill oracle (numpy fp64, one BLAS thread) on 8 tokens of the
+        # 4096 -> 16384 up projection
+        from threadpoolctl import threadpool_limits
+        from oracle import grinqh_oracle
+        rng = np.random.default_rng(4096)
+        q = rng.integers(0, 256, size=(16384, 4096), dtype=np.uint8)
+        s_ = rng.uniform(0.001, 0.01, 16384).astype(np.float16)
+        z_ = rng.normal(0, 0.01, 16384).astype(np.float16)
+        xs = S.bf16_bits_to_f32(S.f32_to_bf16_bits(rng.standard_normal((8, 4096)).astype(np.float32)))
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            grinqh_oracle.prefill_gemm(xs, q, s_, z_, 8)
+            el = time.perf_counter() - t0
+        out["prefill"] = {"value": round(8 / el, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                          "TFLOP/s": round(2.0 * 8 * 4096 * 16384 / el / 1e12, 6),
+                          "sample": f"8 tokens through 4096->16384 at b_max 8 (numpy fp64 oracle, one thread, {el:.1f} s)"}
+    return out
 
 
 def main() -> int:
@@ -483,7 +501,7 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(shapes, eff, args.cpu_seconds)
+        cpu = cpu_baseline(shapes, eff, args.cpu_seconds, prefill=not args.no_prefill)
         log(f"cpu baseline: {cpu}")
 
     out = {
