@@ -52,148 +52,127 @@ struct PrefillArgs {
     uint32_t plane_bytes;
 };
 
+// Element offset of (row r, channel chunk c) in a [rows][64] bf16 tile.  The
+// swizzle keeps 8 consecutive rows (MFMA operand reads) on distinct chunks,
+// and the rows a half-wave's code writes touch (word positions 16 and 64
+// outputs apart) on distinct banks.
 __device__ __forceinline__ int tile_off(int r, int c) {
-    return r * kTK + ((c ^ (r & 7) ^ ((r >> 4) & 7)) << 3);
-}
-
-// (channel pair, word position) of plane item i: within every 32 lanes, 8
-// word positions x 4 consecutive pairs, so that the transposing code writes
-// of a half-wave fall on distinct banks and 8 lanes read 32 contiguous bytes
-// of a plane row.
-template <int TN>
-__device__ __forceinline__ int item_word(int i) {
-    if constexpr (TN == 128) return i & 7;
-    else return (i & 7) | (((i >> 5) & 1) << 3);
-}
-template <int TN>
-__device__ __forceinline__ int item_pair(int i) {
-    if constexpr (TN == 128) return i >> 3;
-    else return ((i >> 3) & 3) | ((i >> 6) << 2);
+    return r * kTK + ((c ^ (r & 7) ^ ((r >> 4) & 7) ^ (((r >> 6) & 3) << 1)) << 3);
 }
 
 // One stage's operands in flight.  X: chunk item i = t + 256 u is row i / 8,
-// chunk i % 8.  Planes: item i = t + 256 u is the channel pair item_pair(i)
-// at word position item_word(i), both channels' P plane words.
+// chunk i % 8.  Planes: thread t takes channel k0 + t / 4 and the WPT word
+// positions from (n0 / 16) + (t % 4) WPT, one 4 WPT-byte load per plane.
 template <int P, int TM, int TN>
 struct Stage {
-    static constexpr int XI = TM * 8 / kPThreads;          // X chunks per thread
-    static constexpr int WI = (kTK / 2) * (TN / 16) / kPThreads;   // (pair, word) items per thread
+    static constexpr int XI = TM * 8 / kPThreads;     // X chunks per thread
+    static constexpr int WPT = TN / 64;               // plane words per thread and plane
     u32x4 xr[XI];
-    uint32_t w[WI][2][P];
+    uint32_t pw[P][WPT];
 };
 
 template <int P, int TM, int TN>
-__device__ __forceinline__ void load_stage(Stage<P, TM, TN>& st, const PrefillArgs& a, int n0, int k0,
-                                           __amdgpu_buffer_rsrc_t xrs, __amdgpu_buffer_rsrc_t prs,
-                                           uint32_t row_bytes) {
+struct Merged {
+    uint32_t E[Stage<P, TM, TN>::WPT][4];   // merge_codes words of each word position
+};
+
+template <int P, int TM, int TN, int L>
+__device__ __forceinline__ void load_unit(Stage<P, TM, TN>& st, const PrefillArgs& a, int n0, int k0,
+                                          __amdgpu_buffer_rsrc_t xrs, __amdgpu_buffer_rsrc_t prs,
+                                          uint32_t row_bytes) {
     using St = Stage<P, TM, TN>;
     const int t = threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < St::XI; ++u) {
-        const int i = t + kPThreads * u;
+    if constexpr (L < St::XI) {
+        const int i = t + kPThreads * L;
         const int k = k0 + 8 * (i & 7);
         // rows past M lie past the resource; d_in % 8 == 0, so a chunk is
         // all in or all out of the row
         const uint32_t off = k < a.d_in ? static_cast<uint32_t>((i >> 3) * a.d_in + k) * 2u : kPlaneOutOfRange;
-        st.xr[u] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < St::WI; ++u) {
-        const int i = t + kPThreads * u;
-        const int word = (n0 >> 4) + item_word<TN>(i);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int ch = k0 + 2 * item_pair<TN>(i) + h;
-            const bool ok = ch < a.d_in && word < a.row_words;
-            // inside channel ch's P plane rows, so a plane offset keeps it in the buffer
-            const uint32_t off = ok ? (static_cast<uint32_t>(ch) * P * static_cast<uint32_t>(a.row_words) +
-                                       static_cast<uint32_t>(word)) * 4u
-                                    : kPlaneOutOfRange;
-#pragma unroll
-            for (int p = 0; p < P; ++p)
-                st.w[u][h][p] = __builtin_amdgcn_raw_buffer_load_b32(prs, off, static_cast<uint32_t>(p) * row_bytes, 0);
+        st.xr[L] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+    } else {
+        constexpr int p = L - St::XI;
+        const int ch = k0 + (t >> 2);
+        const int word = (n0 >> 4) + (t & 3) * St::WPT;
+        // row_words is a multiple of 4, so the WPT words are all in or all out;
+        // inside channel ch's plane rows, a plane offset keeps it in the buffer
+        const bool ok = ch < a.d_in && word < a.row_words;
+        const uint32_t off = ok ? (static_cast<uint32_t>(ch) * P * static_cast<uint32_t>(a.row_words) +
+                                   static_cast<uint32_t>(word)) * 4u
+                                : kPlaneOutOfRange;
+        if constexpr (St::WPT == 4) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(prs, off, static_cast<uint32_t>(p) * row_bytes, 0);
+            st.pw[p][0] = v.x; st.pw[p][1] = v.y; st.pw[p][2] = v.z; st.pw[p][3] = v.w;
+        } else {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(prs, off, static_cast<uint32_t>(p) * row_bytes, 0);
+            st.pw[p][0] = v.x; st.pw[p][1] = v.y;
         }
     }
 }
 
-// Decoded plane words of a prefetched stage: per item and channel, the four
-// merge_codes words (byte b of word k: the code of output 4b + k, scaled by
-// the byte lane's constant, undone in the epilogue).
-template <int P, int TM, int TN>
-struct Merged {
-    uint32_t E[Stage<P, TM, TN>::WI][2][4];
-};
-
-template <int P, int TM, int TN>
-__device__ __forceinline__ void merge_stage(const Stage<P, TM, TN>& st, Merged<P, TM, TN>& mg) {
-#pragma unroll
-    for (int u = 0; u < Stage<P, TM, TN>::WI; ++u)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            merge_codes<P>(st.w[u][h], mg.E[u][h]);
-            // hide the known-zero bits so that each byte becomes one
-            // v_cvt_f32_ubyte (this also ends the scheduling region, so the
-            // merges stay ahead of the matrix work)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) asm("" : "+v"(mg.E[u][h][k]));
-        }
+template <int P, int TM, int TN, int L0, int L1>
+__device__ __forceinline__ void load_units(Stage<P, TM, TN>& st, const PrefillArgs& a, int n0, int k0,
+                                           __amdgpu_buffer_rsrc_t xrs, __amdgpu_buffer_rsrc_t prs,
+                                           uint32_t row_bytes) {
+    if constexpr (L0 < L1) {
+        load_unit<P, TM, TN, L0>(st, a, n0, k0, xrs, prs, row_bytes);
+        load_units<P, TM, TN, L0 + 1, L1>(st, a, n0, k0, xrs, prs, row_bytes);
+    }
 }
 
-// Writes a prefetched stage into one LDS buffer: X chunks as they are, and
-// the codes of both channels of a pair as bf16 pairs (the even channel in
-// the low half) at every output of the word position.
-template <int P, int TM, int TN>
-__device__ __forceinline__ void store_stage(const Stage<P, TM, TN>& st, const Merged<P, TM, TN>& mg, uint16_t* xs,
-                                            uint16_t* ws) {
-    using St = Stage<P, TM, TN>;
+// Byte codes of word position V (merge_codes: byte b of word k is the code
+// of output 4b + k times the byte lane's power of two, undone in the
+// epilogue).
+template <int P, int TM, int TN, int V>
+__device__ __forceinline__ void merge_unit(const Stage<P, TM, TN>& st, Merged<P, TM, TN>& mg) {
+    uint32_t w[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) w[p] = st.pw[p][V];
+    merge_codes<P>(w, mg.E[V]);
+    // hide the known-zero bits so that each byte becomes one v_cvt_f32_ubyte
+#pragma unroll
+    for (int k = 0; k < 4; ++k) asm("" : "+v"(mg.E[V][k]));
+}
+
+// Code unit U: output 4b + k of word position v, one bf16 into the code tile
+// (an integer up to 255 is the upper half of its fp32, exactly).
+template <int P, int TM, int TN, int U>
+__device__ __forceinline__ void code_unit(const Merged<P, TM, TN>& mg, uint16_t* ws) {
+    constexpr int WPT = Stage<P, TM, TN>::WPT;
+    constexpr int v = U / 16, k = (U % 16) / 4, b = U % 4;
     const int t = threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < St::XI; ++u) {
-        const int i = t + kPThreads * u;
-        *reinterpret_cast<u32x4*>(xs + tile_off(i >> 3, i & 7)) = st.xr[u];
-    }
-#pragma unroll
-    for (int u = 0; u < St::WI; ++u) {
-        const int i = t + kPThreads * u;
-        const int cp = item_pair<TN>(i);
-        const int chunk = cp >> 2;
-        const int elem = (2 * cp) & 7;
-        const int row0 = 16 * item_word<TN>(i);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float v0 = byte_f32(mg.E[u][0][k], b), v1 = byte_f32(mg.E[u][1][k], b);
-                // integers <= 255: the bf16 is the upper half of the fp32, exactly
-                const uint32_t pair = __builtin_amdgcn_perm(__float_as_uint(v1), __float_as_uint(v0), 0x07060302u);
-                *reinterpret_cast<uint32_t*>(ws + tile_off(row0 + 4 * b + k, chunk) + elem) = pair;
-            }
+    const int c = t >> 2;
+    const int n = 16 * ((t & 3) * WPT + v) + 4 * b + k;
+    const float f = byte_f32(mg.E[v][k], b);
+    ws[tile_off(n, c >> 3) + (c & 7)] = static_cast<uint16_t>(__float_as_uint(f) >> 16);
+}
+
+template <int P, int TM, int TN, int U0, int U1>
+__device__ __forceinline__ void code_units(const Merged<P, TM, TN>& mg, uint16_t* ws) {
+    if constexpr (U0 < U1) {
+        code_unit<P, TM, TN, U0>(mg, ws);
+        code_units<P, TM, TN, U0 + 1, U1>(mg, ws);
     }
 }
 
-// One wave's (TM / 2) x (TN / 2) quarter: FM x FN tiles of 32 x 32.
-template <int FM, int FN>
-__device__ __forceinline__ void mma_stage(f32x16 (&acc)[FM][FN], const uint16_t* xs, const uint16_t* ws,
-                                          int row_a, int row_b, int lane) {
-#pragma unroll
-    for (int kk = 0; kk < kTK / 16; ++kk) {
-        const int c = 2 * kk + (lane >> 5);
-        bf16x8 av[FM], bv[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-            av[i] = *reinterpret_cast<const bf16x8*>(xs + tile_off(row_a + 32 * i + (lane & 31), c));
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            bv[j] = *reinterpret_cast<const bf16x8*>(ws + tile_off(row_b + 32 * j + (lane & 31), c));
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+template <int P, int TM, int TN, int V0, int V1>
+__device__ __forceinline__ void merge_units(const Stage<P, TM, TN>& st, Merged<P, TM, TN>& mg) {
+    if constexpr (V0 < V1) {
+        merge_unit<P, TM, TN, V0>(st, mg);
+        merge_units<P, TM, TN, V0 + 1, V1>(st, mg);
     }
 }
 
-// One k-step's MFMA operands of a wave: FM row fragments of X and FN of the
+template <int P, int TM, int TN, int X0, int X1>
+__device__ __forceinline__ void x_units(const Stage<P, TM, TN>& st, uint16_t* xs) {
+    if constexpr (X0 < X1) {
+        const int i = static_cast<int>(threadIdx.x) + kPThreads * X0;
+        *reinterpret_cast<u32x4*>(xs + tile_off(i >> 3, i & 7)) = st.xr[X0];
+        x_units<P, TM, TN, X0 + 1, X1>(st, xs);
+    }
+}
+
+// One wave's MFMA operands of a k-step: FM row fragments of X and FN of the
 // codes, 8 consecutive channels per lane.
 template <int FM, int FN>
 struct Frag {
@@ -212,57 +191,52 @@ __device__ __forceinline__ void read_frags(Frag<FM, FN>& f, const uint16_t* xs, 
         f.b[j] = *reinterpret_cast<const bf16x8*>(ws + tile_off(row_b + 32 * j + (lane & 31), c));
 }
 
-// Decode unit U of the next stage: output 4b + k of item u's word position,
-// both channels of the pair, one bf16 pair into the LDS code tile.
-template <int P, int TM, int TN, int U>
-__device__ __forceinline__ void code_unit(const Merged<P, TM, TN>& mg, uint16_t* ws) {
-    constexpr int u = U / 16, k = (U % 16) / 4, b = U % 4;
-    const int i = static_cast<int>(threadIdx.x) + kPThreads * u;
-    const int cp = item_pair<TN>(i);
-    const float v0 = byte_f32(mg.E[u][0][k], b), v1 = byte_f32(mg.E[u][1][k], b);
-    // integers <= 255: the bf16 is the upper half of the fp32, exactly
-    const uint32_t pair = __builtin_amdgcn_perm(__float_as_uint(v1), __float_as_uint(v0), 0x07060302u);
-    *reinterpret_cast<uint32_t*>(ws + tile_off(16 * item_word<TN>(i) + 4 * b + k, cp >> 2) + ((2 * cp) & 7)) = pair;
-}
-
-template <int P, int TM, int TN, int U0, int U1>
-__device__ __forceinline__ void code_units(const Merged<P, TM, TN>& mg, uint16_t* ws) {
-    if constexpr (U0 < U1) {
-        code_unit<P, TM, TN, U0>(mg, ws);
-        code_units<P, TM, TN, U0 + 1, U1>(mg, ws);
-    }
-}
-
-template <int P, int TM, int TN, int X0, int X1>
-__device__ __forceinline__ void x_units(const Stage<P, TM, TN>& st, uint16_t* xs) {
-    if constexpr (X0 < X1) {
-        const int i = static_cast<int>(threadIdx.x) + kPThreads * X0;
-        *reinterpret_cast<u32x4*>(xs + tile_off(i >> 3, i & 7)) = st.xr[X0];
-        x_units<P, TM, TN, X0 + 1, X1>(st, xs);
-    }
-}
-
-// MFMA G of a stage (k-step G / (FM FN)), followed by its share of the next
-// stage's decode and X writes, in a fixed order (scheduling fences), so that
-// the decode runs on the vector units while the matrix cores work.  Halfway
-// through a k-step the next k-step's operands are read into the other
-// fragment set.
+// Everything a loop body does besides the barrier, as one fixed sequence
+// (scheduling fences between the steps): MFMA G of the current stage, then
+// its share of the loads of the stage after next, of the merges and code
+// writes of the next stage and of its X writes.  Halfway through a k-step the
+// next k-step's operands are read into the other fragment set.
 template <int G, int P, int TM, int TN>
-__device__ __forceinline__ void step(f32x16 (&acc)[TM / 64][TN / 64], Frag<TM / 64, TN / 64> (&fr)[2],
-                                     const uint16_t* xs, const uint16_t* ws, const Stage<P, TM, TN>& st,
-                                     const Merged<P, TM, TN>& mg, uint16_t* xs_next, uint16_t* ws_next,
+__device__ __forceinline__ void body(f32x16 (&acc)[TM / 64][TN / 64], Frag<TM / 64, TN / 64> (&fr)[2],
+                                     const uint16_t* xs, const uint16_t* ws, const Stage<P, TM, TN>& cur,
+                                     Stage<P, TM, TN>& nxt, Merged<P, TM, TN>& mg, uint16_t* xs_next,
+                                     uint16_t* ws_next, const PrefillArgs& a, int n0, int k_load,
+                                     __amdgpu_buffer_rsrc_t xrs, __amdgpu_buffer_rsrc_t prs, uint32_t row_bytes,
                                      int row_a, int row_b, int lane) {
+    using St = Stage<P, TM, TN>;
     constexpr int FM = TM / 64, FN = TN / 64, PER = FM * FN, NM = PER * (kTK / 16);
     if constexpr (G < NM) {
         constexpr int kk = G / PER, mi = G % PER, i = mi / FN, j = mi % FN;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kk & 1].a[i], fr[kk & 1].b[j], acc[i][j], 0, 0, 0);
         if constexpr (mi == PER / 2 && kk + 1 < kTK / 16)
             read_frags<FM, FN>(fr[(kk + 1) & 1], xs, ws, kk + 1, row_a, row_b, lane);
-        constexpr int NU = Stage<P, TM, TN>::WI * 16, XI = Stage<P, TM, TN>::XI;
-        code_units<P, TM, TN, G * NU / NM, (G + 1) * NU / NM>(mg, ws_next);
-        x_units<P, TM, TN, G * XI / NM, (G + 1) * XI / NM>(st, xs_next);
+        constexpr int NL = St::XI + P;
+        load_units<P, TM, TN, G * NL / NM, (G + 1) * NL / NM>(nxt, a, n0, k_load, xrs, prs, row_bytes);
+        // merges in the first WPT slots, code writes over the rest
+        constexpr int WPT = St::WPT, NU = WPT * 16;
+        if constexpr (G < WPT) merge_units<P, TM, TN, G, G + 1>(cur, mg);
+        if constexpr (G >= WPT)
+            code_units<P, TM, TN, (G - WPT) * NU / (NM - WPT), (G - WPT + 1) * NU / (NM - WPT)>(mg, ws_next);
+        x_units<P, TM, TN, G * St::XI / NM, (G + 1) * St::XI / NM>(cur, xs_next);
         __builtin_amdgcn_sched_barrier(0);
-        step<G + 1, P, TM, TN>(acc, fr, xs, ws, st, mg, xs_next, ws_next, row_a, row_b, lane);
+        body<G + 1, P, TM, TN>(acc, fr, xs, ws, cur, nxt, mg, xs_next, ws_next, a, n0, k_load, xrs, prs, row_bytes,
+                               row_a, row_b, lane);
+    }
+}
+
+// The last stage's matrix work alone.
+template <int FM, int FN>
+__device__ __forceinline__ void mma_stage(f32x16 (&acc)[FM][FN], const uint16_t* xs, const uint16_t* ws,
+                                          int row_a, int row_b, int lane) {
+#pragma unroll
+    for (int kk = 0; kk < kTK / 16; ++kk) {
+        Frag<FM, FN> f;
+        read_frags<FM, FN>(f, xs, ws, kk, row_a, row_b, lane);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
     }
 }
 
@@ -296,28 +270,28 @@ __global__ __launch_bounds__(kPThreads, (TM * TN > 128 * 128 ? 1 : 2)) void pref
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int n_stages = (a.d_in + kTK - 1) / kTK;
+    using St = Stage<P, TM, TN>;
     // Stage s is computed from LDS while stage s + 1, loaded one iteration
     // earlier, is decoded into the other LDS buffer and stage s + 2 is
     // loaded; stages past the last load nothing (out-of-range offsets).
-    Stage<P, TM, TN> sa, sb;
+    St sa, sb;
     Merged<P, TM, TN> mg;
     Frag<FM, FN> fr[2];
-    load_stage<P, TM, TN>(sa, a, n0, 0, xrs, prs, row_bytes);
-    merge_stage<P, TM, TN>(sa, mg);
-    store_stage<P, TM, TN>(sa, mg, xs[0], wsh[0]);
-    load_stage<P, TM, TN>(sa, a, n0, kTK, xrs, prs, row_bytes);
+    load_units<P, TM, TN, 0, St::XI + P>(sa, a, n0, 0, xrs, prs, row_bytes);
+    merge_units<P, TM, TN, 0, St::WPT>(sa, mg);
+    code_units<P, TM, TN, 0, St::WPT * 16>(mg, wsh[0]);
+    x_units<P, TM, TN, 0, St::XI>(sa, xs[0]);
+    load_units<P, TM, TN, 0, St::XI + P>(sa, a, n0, kTK, xrs, prs, row_bytes);
     __syncthreads();
     int s = 0;
     for (; s + 1 < n_stages; s += 2) {
-        load_stage<P, TM, TN>(sb, a, n0, (s + 2) * kTK, xrs, prs, row_bytes);
-        merge_stage<P, TM, TN>(sa, mg);
         read_frags<FM, FN>(fr[0], xs[0], wsh[0], 0, row_a, row_b, lane);
-        step<0, P, TM, TN>(acc, fr, xs[0], wsh[0], sa, mg, xs[1], wsh[1], row_a, row_b, lane);
+        body<0, P, TM, TN>(acc, fr, xs[0], wsh[0], sa, sb, mg, xs[1], wsh[1], a, n0, (s + 2) * kTK, xrs, prs,
+                           row_bytes, row_a, row_b, lane);
         __syncthreads();
-        load_stage<P, TM, TN>(sa, a, n0, (s + 3) * kTK, xrs, prs, row_bytes);
-        merge_stage<P, TM, TN>(sb, mg);
         read_frags<FM, FN>(fr[0], xs[1], wsh[1], 0, row_a, row_b, lane);
-        step<0, P, TM, TN>(acc, fr, xs[1], wsh[1], sb, mg, xs[0], wsh[0], row_a, row_b, lane);
+        body<0, P, TM, TN>(acc, fr, xs[1], wsh[1], sb, sa, mg, xs[0], wsh[0], a, n0, (s + 3) * kTK, xrs, prs,
+                           row_bytes, row_a, row_b, lane);
         __syncthreads();
     }
     if (s < n_stages) mma_stage<FM, FN>(acc, xs[0], wsh[0], row_a, row_b, lane);
