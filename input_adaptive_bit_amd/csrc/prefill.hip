@@ -361,8 +361,10 @@ hipError_t launch_t(PrefillArgs a, hipStream_t stream) {
 }
 
 template <int P>
-hipError_t launch_p(const PrefillArgs& a, bool big, hipStream_t stream) {
-    return big ? launch_t<P, 256, 256>(a, stream) : launch_t<P, 128, 128>(a, stream);
+hipError_t launch_p(const PrefillArgs& a, int tile, hipStream_t stream) {
+    if (tile == 2) return launch_t<P, 256, 256>(a, stream);
+    if (tile == 1) return launch_t<P, 256, 128>(a, stream);
+    return launch_t<P, 128, 128>(a, stream);
 }
 
 long tiles_of(int M, int d_out, int tm, int tn) {
@@ -377,8 +379,9 @@ size_t prefill_workspace_bytes(int M) {
 
 long prefill_tiles(const grinqh_layout& L, int M) { return tiles_of(M, L.d_out, 128, 128); }
 
-// 256 x 256 tiles (one workgroup per CU) once they alone give every CU a
-// workgroup; 128 x 128 tiles (two per CU) for smaller products.
+// Tiles (tokens x outputs): 256 x 256 once they alone give every CU a
+// workgroup, else 256 x 128 once those do (both one workgroup per CU), else
+// 128 x 128 (two per CU) for small products.
 hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, const uint32_t* planes,
                           const uint16_t* s, const uint16_t* z, void* y, int y_dtype, float* rowsum,
                           int cu_count, hipStream_t stream) {
@@ -398,14 +401,14 @@ hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, cons
     a.row_words = L.row_words;
     a.y_dtype = y_dtype;
     a.plane_bytes = static_cast<uint32_t>(static_cast<size_t>(L.d_in) * L.n_planes * L.row_words * 4u);
-    bool big = tiles_of(M, L.d_out, 256, 256) >= cu_count;
-    const int env = env_int("GRINQH_PREFILL_TILE");
-    if (env == 128 || env == 256) big = env == 256;
+    int tile = tiles_of(M, L.d_out, 256, 256) >= cu_count ? 2 : tiles_of(M, L.d_out, 256, 128) >= cu_count ? 1 : 0;
+    const int env = env_int("GRINQH_PREFILL_TILE");   // 128, 256 (256 x 256) or 2561 (256 x 128)
+    if (env == 128 || env == 256 || env == 2561) tile = env == 256 ? 2 : env == 2561 ? 1 : 0;
     switch (L.n_planes) {
-        case 1: return launch_p<1>(a, big, stream);
-        case 2: return launch_p<2>(a, big, stream);
-        case 3: return launch_p<3>(a, big, stream);
-        case 4: return launch_p<4>(a, big, stream);
+        case 1: return launch_p<1>(a, tile, stream);
+        case 2: return launch_p<2>(a, tile, stream);
+        case 3: return launch_p<3>(a, tile, stream);
+        case 4: return launch_p<4>(a, tile, stream);
         default: return hipErrorInvalidValue;
     }
 }

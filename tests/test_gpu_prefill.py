@@ -184,11 +184,12 @@ def test_prefill_full_size_sampled(dev, b_max):
     assert err <= TOL_BF16
 
 
-@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("tile", [128, 256, 2561])
 @pytest.mark.parametrize("b_max", [2, 8])
 def test_prefill_forced_tiles(dev, monkeypatch, tile, b_max):
-    """Both tile sizes, forced through the library's override, on shapes with
-    ragged token, channel and output tails."""
+    """Every tile shape (128 x 128, 256 x 256 and, as 2561, 256 x 128), forced
+    through the library's override, on shapes with ragged token, channel and
+    output tails."""
     import torch
     import input_adaptive_bit_amd as G
     monkeypatch.setenv("GRINQH_PREFILL_TILE", str(tile))
