@@ -193,8 +193,8 @@ __device__ __forceinline__ void read_frags(Frag<FM, FN>& f, const uint16_t* xs, 
 
 // Everything a loop body does besides the barrier, as one fixed sequence
 // (scheduling fences between the steps): MFMA G of the current stage, then
-// its share of the loads of the stage after next, of the merges and code
-// writes of the next stage and of its X writes.  Halfway through a k-step the
+// its share of the loads of the stage after next (over the first half), of the
+// merges and code writes of the next stage and of its X writes.  Halfway through a k-step the
 // next k-step's operands are read into the other fragment set.
 template <int G, int P, int TM, int TN>
 __device__ __forceinline__ void body(f32x16 (&acc)[TM / 64][TN / 64], Frag<TM / 64, TN / 64> (&fr)[2],
@@ -210,8 +210,9 @@ __device__ __forceinline__ void body(f32x16 (&acc)[TM / 64][TN / 64], Frag<TM / 
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kk & 1].a[i], fr[kk & 1].b[j], acc[i][j], 0, 0, 0);
         if constexpr (mi == PER / 2 && kk + 1 < kTK / 16)
             read_frags<FM, FN>(fr[(kk + 1) & 1], xs, ws, kk + 1, row_a, row_b, lane);
-        constexpr int NL = St::XI + P;
-        load_units<P, TM, TN, G * NL / NM, (G + 1) * NL / NM>(nxt, a, n0, k_load, xrs, prs, row_bytes);
+        // loads spread over the first half, so the last has half a stage to arrive
+        constexpr int NL = St::XI + P, NH = NM / 2;
+        if constexpr (G < NH) load_units<P, TM, TN, G * NL / NH, (G + 1) * NL / NH>(nxt, a, n0, k_load, xrs, prs, row_bytes);
         // merges in the first WPT slots, code writes over the rest
         constexpr int WPT = St::WPT, NU = WPT * 16;
         if constexpr (G < WPT) merge_units<P, TM, TN, G, G + 1>(cur, mg);
