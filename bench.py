@@ -210,6 +210,44 @@ def time_graph(g, reps: int = 1) -> float:
     return st.elapsed_time(en)
 
 
+def cpu_baseline_rows():
+    """The oracle on bounded samples of the rows after the decode GEMV."""
+    import synthetic as S
+    rows = {}
+    # the prefill oracle (numpy fp64, one BLAS thread) on 8 tokens of the
+    # 4096 -> 16384 up projection
+    from threadpoolctl import threadpool_limits
+    from oracle import grinqh_oracle
+    rng = np.random.default_rng(4096)
+    q = rng.integers(0, 256, size=(16384, 4096), dtype=np.uint8)
+    s_ = rng.uniform(0.001, 0.01, 16384).astype(np.float16)
+    z_ = rng.normal(0, 0.01, 16384).astype(np.float16)
+    xs = S.bf16_bits_to_f32(S.f32_to_bf16_bits(rng.standard_normal((8, 4096)).astype(np.float32)))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        grinqh_oracle.prefill_gemm(xs, q, s_, z_, 8)
+        el = time.perf_counter() - t0
+    rows["prefill"] = {"value": round(8 / el, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                      "TFLOP/s": round(2.0 * 8 * 4096 * 16384 / el / 1e12, 6),
+                      "sample": f"8 tokens through 4096->16384 at b_max 8 (numpy fp64 oracle, one thread, {el:.1f} s)"}
+    # the offline rows: threshold calibration of 128 x 4096 bf16 samples and
+    # RTN quantisation of a 4096 x 4096 bf16 matrix
+    xc = S.bf16_bits_to_f32(S.f32_to_bf16_bits(rng.standard_t(3, 128 * 4096).astype(np.float32)))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        grinqh_oracle.calibrate_thresholds(xc, [0.2, 0.5, 0.8, 0.95])
+        el_c = time.perf_counter() - t0
+        wq = S.bf16_bits_to_f32(S.f32_to_bf16_bits((rng.standard_normal((4096, 4096)) * 0.02).astype(np.float32)))
+        t0 = time.perf_counter()
+        grinqh_oracle.quantize_rtn(wq, 8)
+        el_r = time.perf_counter() - t0
+    rows["threshold_calibration"] = {"value": round(el_c * 1e6, 1), "unit": "us", "cores": 1, "kind": "oracle",
+                                    "sample": "128 x 4096 bf16 samples, 4 levels (numpy fp64 oracle, one thread)"}
+    rows["rtn_quantisation"] = {"value": round(el_r * 1e6, 1), "unit": "us", "cores": 1, "kind": "oracle",
+                               "sample": "4096 x 4096 bf16 weights at b_max 8 (numpy oracle, one thread)"}
+    return rows
+
+
 def cpu_baseline(shapes, eff, seconds: float, prefill: bool = True):
     from oracle import c_oracle
     per_step = sum(sh.req[eff] for sh in shapes)
@@ -231,22 +269,7 @@ def cpu_baseline(shapes, eff, seconds: float, prefill: bool = True):
                    f"(plain fp64 C oracle, one thread, {el:.1f} s)"),
     }
     if prefill:
-        # the prefill oracle (numpy fp64, one BLAS thread) on 8 tokens of the
-        # 4096 -> 16384 up projection
-        from threadpoolctl import threadpool_limits
-        from oracle import grinqh_oracle
-        rng = np.random.default_rng(4096)
-        q = rng.integers(0, 256, size=(16384, 4096), dtype=np.uint8)
-        s_ = rng.uniform(0.001, 0.01, 16384).astype(np.float16)
-        z_ = rng.normal(0, 0.01, 16384).astype(np.float16)
-        xs = S.bf16_bits_to_f32(S.f32_to_bf16_bits(rng.standard_normal((8, 4096)).astype(np.float32)))
-        with threadpool_limits(limits=1):
-            t0 = time.perf_counter()
-            grinqh_oracle.prefill_gemm(xs, q, s_, z_, 8)
-            el = time.perf_counter() - t0
-        out["prefill"] = {"value": round(8 / el, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                          "TFLOP/s": round(2.0 * 8 * 4096 * 16384 / el / 1e12, 6),
-                          "sample": f"8 tokens through 4096->16384 at b_max 8 (numpy fp64 oracle, one thread, {el:.1f} s)"}
+        out.update(cpu_baseline_rows())
     return out
 
 
