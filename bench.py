@@ -470,12 +470,12 @@ def main() -> int:
             yp = torch.empty((M, do), dtype=torch.bfloat16, device=dev)
             wsp = torch.empty(G.grinqh_prefill_workspace_bytes(M), dtype=torch.uint8, device=dev)
 
-            def pre(reps=4):
+            def pre(reps=16):
                 for _ in range(reps):
                     G.grinqh_prefill_gemm(Lp, xp, pl, sp, zp, yp, wsp)
             g = capture(pre)
             time_graph(g)
-            t = time_graph(g) * 1e3 / 4
+            t = time_graph(g) * 1e3 / 16
             flops = 2.0 * M * di * do
             # the same product on a dense bf16 weight through torch (hipBLASLt), for context
             wd = torch.randn((do, di), generator=gen, device=dev).to(torch.bfloat16)
@@ -484,11 +484,11 @@ def main() -> int:
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            for _ in range(10):
+            for _ in range(20):
                 torch.matmul(xp, wd.t())
             e1.record()
             torch.cuda.synchronize()
-            tt = e0.elapsed_time(e1) * 1e3 / 10
+            tt = e0.elapsed_time(e1) * 1e3 / 20
             prefill[f"{M}x{di}->{do} b_max {bm}"] = {
                 "us": round(t, 2), "TFLOP/s": round(flops / t / 1e6, 1),
                 "frac_of_bf16_mfma_peak": round(flops / t / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
