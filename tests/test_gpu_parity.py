@@ -507,3 +507,56 @@ def test_gemv_group_matches_oracle_and_single_calls(dev, b_max, x_dtype):
             err = O.max_rel_error(got, ref)
             assert err <= TOL_F32, (rep, k, err, _mismatch(got, ref))
             assert O.max_rel_error(got, single.cpu().numpy()) <= 5e-4, (rep, k)
+
+
+@pytest.mark.parametrize("d_in,d_out,b_max", [(1 << 20, 64, 8), (16, 1 << 20, 4)])
+def test_gemv_maximum_dimensions(dev, d_in, d_out, b_max):
+    """The largest d_in and d_out the library accepts (2^20): thousands of
+    slices accumulating into one tile, and thousands of tiles of one slice."""
+    import torch
+    say(f"gemv maximum dimensions {d_in}->{d_out} b_max={b_max}")
+    g = torch.Generator(device=dev)
+    g.manual_seed(d_in + d_out)
+    q_d = torch.randint(0, 1 << b_max, (d_out, d_in), dtype=torch.uint8, device=dev, generator=g)
+    rng = np.random.default_rng(d_in + d_out)
+    s = rng.uniform(0.001, 0.01, d_out).astype(np.float16)
+    z = rng.normal(0, 0.01, d_out).astype(np.float16)
+    x = S.bf16_bits_to_f32(S.f32_to_bf16_bits(rng.standard_t(3, d_in).astype(np.float32)))
+    theta = np.sort(np.quantile(np.abs(x), np.linspace(0.2, 0.9, b_max // 2))).astype(np.float32)
+    dl = DeviceLinear(None, s, z, b_max, dev, q_dev=q_d)
+    y = dl.gemv(to_dev_x(x, "bf16", dev), _theta_dev(theta, dev), torch.float32)
+    torch.cuda.synchronize()
+    ref = C.gemv(x, theta, q_d.cpu().numpy(), s, z, b_max)
+    err = O.max_rel_error(y.cpu().numpy(), ref)
+    say(f"  max rel err {err:.3e}")
+    assert err <= TOL_F32, (err, _mismatch(y.cpu().numpy(), ref))
+
+
+def test_gemv_group_of_eight(dev):
+    """A group of the maximum size (8 members), ragged shapes, against the oracle."""
+    import torch
+    import input_adaptive_bit_amd as G
+    rng = np.random.default_rng(88)
+    shapes = [(4096, 4096), (1, 1), (777, 1000), (64, 65), (3000, 130), (8, 4100), (14336, 256), (129, 64)]
+    members, ops, refs = [], [], []
+    say("group launch of 8 members")
+    for di, do in shapes:
+        q = rng.integers(0, 256, size=(do, di), dtype=np.uint8)
+        s = rng.uniform(0.001, 0.01, do).astype(np.float16)
+        z = rng.normal(0, 0.01, do).astype(np.float16)
+        x = S.bf16_bits_to_f32(S.f32_to_bf16_bits(rng.standard_t(3, di).astype(np.float32)))
+        theta = np.sort(np.quantile(np.abs(x), (0.2, 0.5, 0.8, 0.95))).astype(np.float32)
+        dl = DeviceLinear(q, s, z, 8, dev)
+        members.append(dl)
+        ops.append((to_dev_x(x, "bf16", dev), _theta_dev(theta, dev), dl.planes, dl.s, dl.z,
+                    torch.empty(do, dtype=torch.float32, device=dev)))
+        refs.append(C.gemv(x, theta, q, s, z, 8))
+    layouts = [m.L for m in members]
+    ws = G.new_group_workspace(layouts, dev)
+    for rep in range(2):
+        G.grinqh_gemv_group(layouts, ops, ws)
+        torch.cuda.synchronize()
+        for k, (o, ref) in enumerate(zip(ops, refs)):
+            got = o[5].cpu().numpy()
+            err = O.max_rel_error(got, ref)
+            assert err <= TOL_F32, (rep, k, err, _mismatch(got, ref))

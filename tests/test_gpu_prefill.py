@@ -203,3 +203,22 @@ def test_prefill_forced_tiles(dev, monkeypatch, tile, b_max):
         torch.cuda.synchronize()
         err = _row_err(y.cpu().numpy().astype(np.float64), O.prefill_gemm(Xh, q, s, z, b_max))
         assert err <= TOL_F32, (M, d_in, d_out, err)
+
+
+def test_prefill_maximum_token_count(dev):
+    """2^20 tokens (the largest M the library accepts) through a narrow layer;
+    sampled rows, the first and last among them, against the oracle."""
+    import torch
+    import input_adaptive_bit_amd as G
+    M, d_in, d_out = 1 << 20, 8, 64
+    say(f"prefill maximum token count M={M} {d_in}->{d_out}")
+    rng = np.random.default_rng(20)
+    q, s, z, X = _inputs(rng, M, d_in, d_out, 8)
+    dl = DeviceLinear(q, s, z, 8, dev)
+    xd, Xh = _x_dev(X, dev)
+    y = G.prefill_gemm(dl.L, xd, dl.planes, dl.s, dl.z, torch.float32)
+    torch.cuda.synchronize()
+    rows = np.sort(np.concatenate([[0, 255, 256, M - 1], rng.choice(M, 60, replace=False)]))
+    R = O.prefill_gemm(Xh[rows], q, s, z, 8)
+    Y = y[torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
+    assert _row_err(Y, R) <= TOL_F32
