@@ -91,3 +91,29 @@ def test_calibration_workspace_reuse(dev):
     for n in (50000, 37, 50000):
         x = rng.standard_t(3, n).astype(np.float32)
         _check(x, list(S.QUANTILES_B8[4]), "f32", dev, ws)
+
+
+def test_calibration_graph_replays(dev):
+    """Calibration captured in a HIP graph (its workspace is initialised by a
+    kernel, no memset): every replay, with eager work in between, gives the
+    oracle's thresholds bit for bit."""
+    import input_adaptive_bit_amd as G
+    import torch
+    rng = np.random.default_rng(12)
+    x = rng.standard_t(3, 128 * 1024).astype(np.float32)
+    xd, xh = _device_x(x, "bf16", dev)
+    lv = list(S.QUANTILES_B8[3])
+    ref = O.calibrate_thresholds(xh, lv)
+    ws = torch.empty(G.grinqh_calibrate_workspace_bytes(), dtype=torch.uint8, device=dev)
+    th = torch.empty(len(lv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        G.grinqh_calibrate_thresholds(xd, lv, th, ws)
+    for rep in range(5):
+        th.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(th.cpu().numpy().view(np.int32), ref.view(np.int32)), rep
+        _check(rng.standard_t(3, 5000).astype(np.float32), [0.5], "f32", dev)     # eager work in between

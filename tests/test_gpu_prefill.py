@@ -222,3 +222,36 @@ def test_prefill_maximum_token_count(dev):
     R = O.prefill_gemm(Xh[rows], q, s, z, 8)
     Y = y[torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
     assert _row_err(Y, R) <= TOL_F32
+
+
+def test_prefill_graph_replays_match_eager(dev):
+    """The prefill call captured in a HIP graph: every replay, with eager work
+    and synchronisations in between, equals the eager call bit for bit (no
+    atomics: the summation order is fixed) and the oracle to tolerance."""
+    import torch
+    import input_adaptive_bit_amd as G
+    rng = np.random.default_rng(30)
+    M, d_in, d_out = 600, 1024, 1500
+    q, s, z, X = _inputs(rng, M, d_in, d_out, 8)
+    dl = DeviceLinear(q, s, z, 8, dev)
+    xd, Xh = _x_dev(X, dev)
+    say("prefill graph replays")
+    eager = G.prefill_gemm(dl.L, xd, dl.planes, dl.s, dl.z, torch.float32)
+    R = O.prefill_gemm(Xh, q, s, z, 8)
+    y = torch.empty((M, d_out), dtype=torch.float32, device=dev)
+    ws = torch.empty(G.grinqh_prefill_workspace_bytes(M), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        G.grinqh_prefill_gemm(dl.L, xd, dl.planes, dl.s, dl.z, y, ws)
+    ref = eager.cpu().numpy()
+    for rep in range(5):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        assert np.array_equal(got, ref), rep
+        assert _row_err(got.astype(np.float64), R) <= TOL_F32, rep
+        _ = G.prefill_gemm(dl.L, xd, dl.planes, dl.s, dl.z, torch.float32)   # eager work between replays
+        torch.cuda.synchronize()

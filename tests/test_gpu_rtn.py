@@ -120,3 +120,31 @@ def test_rtn_then_decode_gemv(dev, b_max):
     err = O.max_rel_error(y.cpu().numpy(), ref)
     say(f"  rtn -> gemv b_max={b_max}: max rel err {err:.3e}")
     assert err <= TOL_F32
+
+
+def test_rtn_graph_replays(dev):
+    """RTN captured in a HIP graph: every replay, with eager work in between,
+    gives the oracle's codes, scales and zero points bit for bit."""
+    import input_adaptive_bit_amd as G
+    import torch
+    rng = np.random.default_rng(13)
+    w = rng.normal(0, 0.02, size=(300, 2048)).astype(np.float32)
+    bits, wf = _bf16(w)
+    wd = torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+    qr, sr, zr = O.quantize_rtn(wf, 8)
+    q = torch.empty((300, 2048), dtype=torch.uint8, device=dev)
+    s = torch.empty(300, dtype=torch.float16, device=dev)
+    z = torch.empty(300, dtype=torch.float16, device=dev)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        G.grinqh_quantize_rtn(wd, 8, q, s, z)
+    for rep in range(5):
+        q.fill_(0)
+        s.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(q.cpu().numpy(), qr), rep
+        assert _same_f16(s.cpu().numpy(), sr) and _same_f16(z.cpu().numpy(), zr), rep
+        _check(rng.normal(size=(7, 100)).astype(np.float32), 4, dev)             # eager work in between
