@@ -255,3 +255,28 @@ def test_prefill_graph_replays_match_eager(dev):
         assert _row_err(got.astype(np.float64), R) <= TOL_F32, rep
         _ = G.prefill_gemm(dl.L, xd, dl.planes, dl.s, dl.z, torch.float32)   # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_prefill_nan_and_inf_rows(dev):
+    """A token row holding NaN or Inf gives non-finite outputs, as in the
+    oracle; the other rows are unaffected."""
+    import torch
+    import input_adaptive_bit_amd as G
+    rng = np.random.default_rng(31)
+    M, d_in, d_out = 40, 512, 300
+    q, s, z, X = _inputs(rng, M, d_in, d_out, 8)
+    X[3, 17] = np.nan
+    X[7, 200] = np.inf
+    X[11, 5] = -np.inf
+    dl = DeviceLinear(q, s, z, 8, dev)
+    xd, Xh = _x_dev(X, dev)
+    y = G.prefill_gemm(dl.L, xd, dl.planes, dl.s, dl.z, torch.float32)
+    torch.cuda.synchronize()
+    Y = y.cpu().numpy().astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        R = O.prefill_gemm(Xh, q, s, z, 8)
+    bad = [3, 7, 11]
+    assert np.all(~np.isfinite(Y[bad])) and np.all(~np.isfinite(R[bad]))
+    good = [m for m in range(M) if m not in bad]
+    assert np.all(np.isfinite(Y[good]))
+    assert _row_err(Y[good], R[good]) <= TOL_F32
