@@ -10,22 +10,21 @@
 // (q <= 255, exact in bf16), so it runs on the bf16 matrix cores with fp32
 // accumulation (v_mfma_f32_32x32x16_bf16); S comes from a row-sum pass.
 //
-// Tiling.  A workgroup computes a T x T tile of Y (T = 256, one workgroup per
-// CU, accumulators in AGPRs; or T = 128, two per CU) and walks the input
-// channels in stages of 64.  Its four waves own (T/2) x (T/2) quarters of
-// 32 x 32 MFMA tiles.  Every thread holds, two stages ahead, 16-byte chunks
-// of X and the P plane words of a channel pair at one 16-output word
-// position.  While the matrix cores work on stage s, the waves decode stage
-// s + 1 (merge_codes, shared with the decode GEMV, then one byte conversion
-// per code and one permute per bf16 channel pair) into the other half of a
-// double-buffered LDS tile: each MFMA is followed, in a fixed order, by its
-// share of that work.
+// Tiling.  A workgroup computes a TM x TN (tokens x outputs) tile of Y --
+// 256 x 256 or 256 x 128 with one workgroup per CU and the accumulators in
+// AGPRs, or 128 x 128 with two per CU -- and walks the input channels in
+// stages of 64.  Its four waves own (TM/2) x (TN/2) quarters of 32 x 32 MFMA
+// tiles.  Every thread holds, two stages ahead, 16-byte chunks of X and, for
+// one channel, the TN/64 plane words of consecutive word positions (one wide
+// load per plane).  While the matrix cores work on stage s, the waves decode
+// stage s + 1 (merge_codes, shared with the decode GEMV, then one byte
+// conversion per code, whose fp32 upper half is the code's bf16) into the
+// other half of a double-buffered LDS tile: each MFMA is followed, in a fixed
+// order, by its share of that work and of the loads.
 //
-// LDS tiles are [T rows][64 channels] of bf16, rows of 8 16-byte chunks,
-// with chunk c of row r stored at chunk c ^ (r & 7) ^ ((r >> 4) & 7): the
-// MFMA operand reads (8 consecutive rows, one chunk) and the transposing
-// code writes (one row per word position, a chunk of four channel pairs)
-// both spread over all banks.
+// LDS tiles are [rows][64 channels] of bf16, rows of 8 16-byte chunks, with
+// the chunks of a row permuted by tile_off below, so that the MFMA operand
+// reads and the transposing code writes spread over all banks.
 #include "decode.hpp"
 #include "device_common.hpp"
 #include "internal.h"
