@@ -212,7 +212,7 @@ grinqh_status grinqh_calibrate_thresholds(const void* x, grinqh_dtype x_dtype, i
  *   w     bf16 [d_out][d_in]: row j holds output channel j's weights.
  *   q     uint8 [d_out][d_in] out.
  *   s, z  fp16 [d_out] out.
- * d_in >= 1, 1 <= d_out <= 2^30, b_max in {2, 4, 6, 8}. */
+ * 1 <= d_in <= 2^30, 1 <= d_out <= 2^30, b_max in {2, 4, 6, 8}. */
 grinqh_status grinqh_quantize_rtn(int32_t d_in, int32_t d_out, int32_t b_max, const uint16_t* w,
                                   uint8_t* q, uint16_t* s, uint16_t* z, void* stream);
 

@@ -112,7 +112,7 @@ using namespace grinqh;
 extern "C" grinqh_status grinqh_quantize_rtn(int32_t d_in, int32_t d_out, int32_t b_max, const uint16_t* w,
                                              uint8_t* q, uint16_t* s, uint16_t* z, void* stream) {
     if (w == nullptr || q == nullptr || s == nullptr || z == nullptr) return GRINQH_EINVAL;
-    if (d_in < 1 || d_out < 1 || d_out > (1 << 30)) return GRINQH_EINVAL;
+    if (d_in < 1 || d_in > (1 << 30) || d_out < 1 || d_out > (1 << 30)) return GRINQH_EINVAL;
     if (b_max != 2 && b_max != 4 && b_max != 6 && b_max != 8) return GRINQH_EINVAL;
     if (reinterpret_cast<uintptr_t>(w) % 2 != 0 || reinterpret_cast<uintptr_t>(s) % 2 != 0 ||
         reinterpret_cast<uintptr_t>(z) % 2 != 0)

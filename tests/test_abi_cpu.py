@@ -203,6 +203,7 @@ def test_rtn_argument_checks_before_any_device_call():
     assert call(d_in=0) == B.GRINQH_EINVAL
     assert call(d_out=0) == B.GRINQH_EINVAL
     assert call(d_out=(1 << 30) + 1) == B.GRINQH_EINVAL
+    assert call(d_in=(1 << 30) + 1) == B.GRINQH_EINVAL          # keeps the kernel's 32-bit row index in range
     for b in (0, 1, 3, 5, 7, 9, 10):
         assert call(b=b) == B.GRINQH_EINVAL, b
     assert call(w=W + 1) == B.GRINQH_EALIGN
