@@ -22,9 +22,10 @@
 // other half of a double-buffered LDS tile: each MFMA is followed, in a fixed
 // order, by its share of that work and of the loads.
 //
-// LDS tiles are [rows][64 channels] of bf16, rows of 8 16-byte chunks, with
-// the chunks of a row permuted by tile_off below, so that the MFMA operand
-// reads and the transposing code writes spread over all banks.
+// The X tile is [tokens][64 channels] of bf16 (rows of 8 16-byte chunks,
+// permuted by tile_off); the code tile is [64 channels][TN outputs] (chunks
+// permuted by code_off), written 8 outputs at a time and read into the B
+// operand with transposing LDS reads (ds_read_b64_tr_b16).
 #include "decode.hpp"
 #include "device_common.hpp"
 #include "internal.h"
@@ -51,12 +52,40 @@ struct PrefillArgs {
     uint32_t plane_bytes;
 };
 
-// Element offset of (row r, channel chunk c) in a [rows][64] bf16 tile.  The
-// swizzle keeps 8 consecutive rows (MFMA operand reads) on distinct chunks,
-// and the rows a half-wave's code writes touch (word positions 16 and 64
-// outputs apart) on distinct banks.
+// Element offset of (row r, channel chunk c) in the [tokens][64] bf16 X
+// tile.  Rows are 128 bytes; chunk c of row r sits at c ^ (r % 8) ^ (bit 3
+// of r), so that 8 consecutive rows (an MFMA operand read, 8 lanes) fall on
+// distinct chunks and 16 consecutive rows on distinct 16-byte bank groups
+// of a 256-byte span.
 __device__ __forceinline__ int tile_off(int r, int c) {
-    return r * kTK + ((c ^ (r & 7) ^ ((r >> 4) & 7) ^ (((r >> 6) & 3) << 1)) << 3);
+    return r * kTK + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 3);
+}
+
+// Element offset of (channel k, output n) in the [64][TN] bf16 code tile: one
+// row per channel (a multiple of 256 bytes), outputs in 16-byte chunks.  With
+// r = k % 4, chunk c sits at c ^ 4r ^ e, e = a + 2 (a ^ bit 3 of c) and
+// a = parity of r ^ (bit 4 of c).  Both access patterns then touch every
+// bank once per 128 bytes: the transposing reads of a 16-lane group (4
+// channels x 16 outputs) and the 16-byte code writes of 8 lanes (2 channels
+// x 4 thread quarters), and likewise per 256 bytes.
+template <int TN>
+__device__ __forceinline__ int code_off(int k, int n) {
+    const int c = n >> 3, r = k & 3;
+    const int par = (r ^ (r >> 1) ^ (c >> 4)) & 1;
+    const int e = par | (((par ^ (c >> 3)) & 1) << 1);
+    return k * TN + ((c ^ (r << 2) ^ e) << 3) + (n & 7);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// 4 consecutive channels for one output per lane (ds_read_b64_tr_b16): in each
+// 16-lane group, lane i supplies the address of channel k0 + i / 4, outputs
+// n0 + 4 (i % 4) .. + 3, and receives channels k0 .. k0 + 3 of output n0 + i.
+template <int TN>
+__device__ __forceinline__ s16x4 read_codes_tr(const uint16_t* ws, int k0, int n0, int i) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(ws + code_off<TN>(k0 + (i >> 2), n0 + 4 * (i & 3))));
 }
 
 // One stage's operands in flight.  X: chunk item i = t + 256 u is row i / 8,
@@ -133,17 +162,25 @@ __device__ __forceinline__ void merge_unit(const Stage<P, TM, TN>& st, Merged<P,
     for (int k = 0; k < 4; ++k) asm("" : "+v"(mg.E[V][k]));
 }
 
-// Code unit U: output 4b + k of word position v, one bf16 into the code tile
-// (an integer up to 255 is the upper half of its fp32, exactly).
+// Code unit U: half h of word position v (outputs 8h .. 8h + 7 of the
+// word), this thread's channel, one 16-byte write of four bf16 pairs (an
+// integer up to 255 is the upper half of its fp32, exactly).
 template <int P, int TM, int TN, int U>
 __device__ __forceinline__ void code_unit(const Merged<P, TM, TN>& mg, uint16_t* ws) {
     constexpr int WPT = Stage<P, TM, TN>::WPT;
-    constexpr int v = U / 16, k = (U % 16) / 4, b = U % 4;
+    constexpr int v = U / 2, h = U % 2;
     const int t = threadIdx.x;
-    const int c = t >> 2;
-    const int n = 16 * ((t & 3) * WPT + v) + 4 * b + k;
-    const float f = byte_f32(mg.E[v][k], b);
-    ws[tile_off(n, c >> 3) + (c & 7)] = static_cast<uint16_t>(__float_as_uint(f) >> 16);
+    uint32_t d[4];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)          // byte b = 2h + e: outputs 4b .. 4b + 3
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) { // outputs 4b + 2pr, 4b + 2pr + 1
+            const float lo = byte_f32(mg.E[v][2 * pr], 2 * h + e);
+            const float hi = byte_f32(mg.E[v][2 * pr + 1], 2 * h + e);
+            d[2 * e + pr] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+        }
+    const int n = 16 * ((t & 3) * WPT + v) + 8 * h;
+    *reinterpret_cast<u32x4*>(ws + code_off<TN>(t >> 2, n)) = u32x4{d[0], d[1], d[2], d[3]};
 }
 
 template <int P, int TM, int TN, int U0, int U1>
@@ -181,13 +218,21 @@ struct Frag {
 template <int FM, int FN>
 __device__ __forceinline__ void read_frags(Frag<FM, FN>& f, const uint16_t* xs, const uint16_t* ws, int kk,
                                            int row_a, int row_b, int lane) {
+    constexpr int TN = 64 * FN;
     const int c = 2 * kk + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
         f.a[i] = *reinterpret_cast<const bf16x8*>(xs + tile_off(row_a + 32 * i + (lane & 31), c));
+    // lane l takes channels 16 kk + 8 (l / 32) .. + 7 of output 32 j + l % 32
+    const int k0 = 16 * kk + 8 * (lane >> 5);
+    const int nl = 16 * ((lane >> 4) & 1);
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-        f.b[j] = *reinterpret_cast<const bf16x8*>(ws + tile_off(row_b + 32 * j + (lane & 31), c));
+    for (int j = 0; j < FN; ++j) {
+        const s16x4 r0 = read_codes_tr<TN>(ws, k0, row_b + 32 * j + nl, lane & 15);
+        const s16x4 r1 = read_codes_tr<TN>(ws, k0 + 4, row_b + 32 * j + nl, lane & 15);
+        const s16x8 w8 = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+        f.b[j] = __builtin_bit_cast(bf16x8, w8);
+    }
 }
 
 // Everything a loop body does besides the barrier, as one fixed sequence
@@ -213,7 +258,7 @@ __device__ __forceinline__ void body(f32x16 (&acc)[TM / 64][TN / 64], Frag<TM / 
         constexpr int NL = St::XI + P, NH = NM / 2;
         if constexpr (G < NH) load_units<P, TM, TN, G * NL / NH, (G + 1) * NL / NH>(nxt, a, n0, k_load, xrs, prs, row_bytes);
         // merges in the first WPT slots, code writes over the rest
-        constexpr int WPT = St::WPT, NU = WPT * 16;
+        constexpr int WPT = St::WPT, NU = WPT * 2;
         if constexpr (G < WPT) merge_units<P, TM, TN, G, G + 1>(cur, mg);
         if constexpr (G >= WPT)
             code_units<P, TM, TN, (G - WPT) * NU / (NM - WPT), (G - WPT + 1) * NU / (NM - WPT)>(mg, ws_next);
@@ -279,7 +324,7 @@ __global__ __launch_bounds__(kPThreads, (TM * TN > 128 * 128 ? 1 : 2)) void pref
     Frag<FM, FN> fr[2];
     load_units<P, TM, TN, 0, St::XI + P>(sa, a, n0, 0, xrs, prs, row_bytes);
     merge_units<P, TM, TN, 0, St::WPT>(sa, mg);
-    code_units<P, TM, TN, 0, St::WPT * 16>(mg, wsh[0]);
+    code_units<P, TM, TN, 0, St::WPT * 2>(mg, wsh[0]);
     x_units<P, TM, TN, 0, St::XI>(sa, xs[0]);
     load_units<P, TM, TN, 0, St::XI + P>(sa, a, n0, kTK, xrs, prs, row_bytes);
     __syncthreads();
