@@ -11,12 +11,13 @@
 // accumulation (v_mfma_f32_32x32x16_bf16); S comes from a row-sum pass.
 //
 // Tiling.  A workgroup computes a TM x TN (tokens x outputs) tile of Y --
-// 256 x 256 or 256 x 128 with one workgroup per CU and the accumulators in
-// AGPRs, or 128 x 128 with two per CU -- and walks the input channels in
-// stages of 64.  Its four waves own (TM/2) x (TN/2) quarters of 32 x 32 MFMA
-// tiles.  Every thread holds, two stages ahead, 16-byte chunks of X and, for
-// one channel, the TN/64 plane words of consecutive word positions (one wide
-// load per plane).  While the matrix cores work on stage s, the waves decode
+// 256 x 256 or 256 x 128 with eight waves (two per SIMD, so that one wave's
+// waits are covered by the other's matrix work), or 128 x 128 with four
+// waves and two workgroups per CU -- and walks the input channels in stages
+// of 64.  The waves form a grid over the tile, each owning a block of 32 x 32
+// MFMA tiles (128 x 64, 64 x 64 and 64 x 64 tokens x outputs).  Every thread
+// holds, two stages ahead, 16-byte chunks of X and, for one channel, 1, 2 or
+// 4 plane words of consecutive word positions (one load per plane).  While the matrix cores work on stage s, the waves decode
 // stage s + 1 (merge_codes, shared with the decode GEMV, then one byte
 // conversion per code, whose fp32 upper half is the code's bf16) into the
 // other half of a double-buffered LDS tile: each MFMA is followed, in a fixed
@@ -34,7 +35,15 @@ namespace grinqh {
 namespace {
 
 constexpr int kTK = 64;                  // input channels per stage
-constexpr int kPThreads = 256;           // 4 waves, 2 x 2 quarters of the tile
+// Waves per workgroup: 8 for the 256-token tiles (two per SIMD), else 4.
+// The waves form a WM x WN grid over the tile; the wave grid is 2 x 2 with
+// four waves and (8 / WN) x WN, WN = TN / 64, with eight.
+__host__ __device__ constexpr int tile_waves(int TM, int TN) { return TM == 256 ? 8 : 4; }
+__host__ __device__ constexpr int tile_wn(int TM, int TN) { return tile_waves(TM, TN) == 4 ? 2 : TN / 64; }
+__host__ __device__ constexpr int tile_wm(int TM, int TN) { return tile_waves(TM, TN) / tile_wn(TM, TN); }
+// 32 x 32 MFMA tiles per wave along the tokens and the outputs
+__host__ __device__ constexpr int tile_fm(int TM, int TN) { return TM / tile_wm(TM, TN) / 32; }
+__host__ __device__ constexpr int tile_fn(int TM, int TN) { return TN / tile_wn(TM, TN) / 32; }
 constexpr uint32_t kPlaneOutOfRange = 0x80000000u;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -93,8 +102,12 @@ __device__ __forceinline__ s16x4 read_codes_tr(const uint16_t* ws, int k0, int n
 // positions from (n0 / 16) + (t % 4) WPT, one 4 WPT-byte load per plane.
 template <int P, int TM, int TN>
 struct Stage {
-    static constexpr int XI = TM * 8 / kPThreads;     // X chunks per thread
-    static constexpr int WPT = TN / 64;               // plane words per thread and plane
+    static constexpr int NT = 64 * tile_waves(TM, TN);  // threads
+    static constexpr int WN = tile_wn(TM, TN), WM = tile_wm(TM, TN);  // wave grid
+    static constexpr int FM = tile_fm(TM, TN), FN = tile_fn(TM, TN);
+    static constexpr int TPC = NT / kTK;                // threads per input channel
+    static constexpr int XI = TM * 8 / NT;              // X chunks per thread
+    static constexpr int WPT = TN / 16 / TPC;           // plane words per thread and plane
     u32x4 xr[XI];
     uint32_t pw[P][WPT];
 };
@@ -111,7 +124,7 @@ __device__ __forceinline__ void load_unit(Stage<P, TM, TN>& st, const PrefillArg
     using St = Stage<P, TM, TN>;
     const int t = threadIdx.x;
     if constexpr (L < St::XI) {
-        const int i = t + kPThreads * L;
+        const int i = t + St::NT * L;
         const int k = k0 + 8 * (i & 7);
         // rows past M lie past the resource; d_in % 8 == 0, so a chunk is
         // all in or all out of the row
@@ -119,8 +132,8 @@ __device__ __forceinline__ void load_unit(Stage<P, TM, TN>& st, const PrefillArg
         st.xr[L] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
     } else {
         constexpr int p = L - St::XI;
-        const int ch = k0 + (t >> 2);
-        const int word = (n0 >> 4) + (t & 3) * St::WPT;
+        const int ch = k0 + t / St::TPC;
+        const int word = (n0 >> 4) + (t % St::TPC) * St::WPT;
         // row_words is a multiple of 4, so the WPT words are all in or all out;
         // inside channel ch's plane rows, a plane offset keeps it in the buffer
         const bool ok = ch < a.d_in && word < a.row_words;
@@ -130,10 +143,13 @@ __device__ __forceinline__ void load_unit(Stage<P, TM, TN>& st, const PrefillArg
         if constexpr (St::WPT == 4) {
             const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(prs, off, static_cast<uint32_t>(p) * row_bytes, 0);
             st.pw[p][0] = v.x; st.pw[p][1] = v.y; st.pw[p][2] = v.z; st.pw[p][3] = v.w;
-        } else {
+        } else if constexpr (St::WPT == 2) {
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
             const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(prs, off, static_cast<uint32_t>(p) * row_bytes, 0);
             st.pw[p][0] = v.x; st.pw[p][1] = v.y;
+        } else {
+            static_assert(St::WPT == 1, "one, two or four plane words per thread");
+            st.pw[p][0] = __builtin_amdgcn_raw_buffer_load_b32(prs, off, static_cast<uint32_t>(p) * row_bytes, 0);
         }
     }
 }
@@ -179,8 +195,9 @@ __device__ __forceinline__ void code_unit(const Merged<P, TM, TN>& mg, uint16_t*
             const float hi = byte_f32(mg.E[v][2 * pr + 1], 2 * h + e);
             d[2 * e + pr] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
         }
-    const int n = 16 * ((t & 3) * WPT + v) + 8 * h;
-    *reinterpret_cast<u32x4*>(ws + code_off<TN>(t >> 2, n)) = u32x4{d[0], d[1], d[2], d[3]};
+    constexpr int TPC = Stage<P, TM, TN>::TPC;
+    const int n = 16 * ((t % TPC) * WPT + v) + 8 * h;
+    *reinterpret_cast<u32x4*>(ws + code_off<TN>(t / TPC, n)) = u32x4{d[0], d[1], d[2], d[3]};
 }
 
 template <int P, int TM, int TN, int U0, int U1>
@@ -202,7 +219,7 @@ __device__ __forceinline__ void merge_units(const Stage<P, TM, TN>& st, Merged<P
 template <int P, int TM, int TN, int X0, int X1>
 __device__ __forceinline__ void x_units(const Stage<P, TM, TN>& st, uint16_t* xs) {
     if constexpr (X0 < X1) {
-        const int i = static_cast<int>(threadIdx.x) + kPThreads * X0;
+        const int i = static_cast<int>(threadIdx.x) + Stage<P, TM, TN>::NT * X0;
         *reinterpret_cast<u32x4*>(xs + tile_off(i >> 3, i & 7)) = st.xr[X0];
         x_units<P, TM, TN, X0 + 1, X1>(st, xs);
     }
@@ -212,48 +229,61 @@ __device__ __forceinline__ void x_units(const Stage<P, TM, TN>& st, uint16_t* xs
 // codes, 8 consecutive channels per lane.
 template <int FM, int FN>
 struct Frag {
-    bf16x8 a[FM], b[FN];
+    bf16x8 a[FM];      // one set, each reloaded for the next k-step after its last use
+    bf16x8 b[2][FN];   // two sets, by k-step parity
 };
 
-template <int FM, int FN>
-__device__ __forceinline__ void read_frags(Frag<FM, FN>& f, const uint16_t* xs, const uint16_t* ws, int kk,
-                                           int row_a, int row_b, int lane) {
-    constexpr int TN = 64 * FN;
-    const int c = 2 * kk + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-        f.a[i] = *reinterpret_cast<const bf16x8*>(xs + tile_off(row_a + 32 * i + (lane & 31), c));
-    // lane l takes channels 16 kk + 8 (l / 32) .. + 7 of output 32 j + l % 32
+// Lane l takes channels 16 kk + 8 (l / 32) .. + 7 of token row + l % 32.
+__device__ __forceinline__ bf16x8 read_a(const uint16_t* xs, int kk, int row, int lane) {
+    return *reinterpret_cast<const bf16x8*>(xs + tile_off(row + (lane & 31), 2 * kk + (lane >> 5)));
+}
+
+// Lane l takes channels 16 kk + 8 (l / 32) .. + 7 of output col + l % 32.
+template <int TN>
+__device__ __forceinline__ bf16x8 read_b(const uint16_t* ws, int kk, int col, int lane) {
     const int k0 = 16 * kk + 8 * (lane >> 5);
-    const int nl = 16 * ((lane >> 4) & 1);
+    const int n0 = col + 16 * ((lane >> 4) & 1);
+    const s16x4 r0 = read_codes_tr<TN>(ws, k0, n0, lane & 15);
+    const s16x4 r1 = read_codes_tr<TN>(ws, k0 + 4, n0, lane & 15);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int FM, int FN, int TN>
+__device__ __forceinline__ void read_frags(Frag<FM, FN>& f, int set, const uint16_t* xs, const uint16_t* ws,
+                                           int kk, int row_a, int row_b, int lane) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const s16x4 r0 = read_codes_tr<TN>(ws, k0, row_b + 32 * j + nl, lane & 15);
-        const s16x4 r1 = read_codes_tr<TN>(ws, k0 + 4, row_b + 32 * j + nl, lane & 15);
-        const s16x8 w8 = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
-        f.b[j] = __builtin_bit_cast(bf16x8, w8);
-    }
+    for (int i = 0; i < FM; ++i) f.a[i] = read_a(xs, kk, row_a + 32 * i, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) f.b[set][j] = read_b<TN>(ws, kk, row_b + 32 * j, lane);
 }
 
 // Everything a loop body does besides the barrier, as one fixed sequence
 // (scheduling fences between the steps): MFMA G of the current stage, then
 // its share of the loads of the stage after next (over the first half), of the
-// merges and code writes of the next stage and of its X writes.  Halfway through a k-step the
-// next k-step's operands are read into the other fragment set.
+// merges and code writes of the next stage and of its X writes.  Each A
+// fragment is reloaded for the next k-step right after its last MFMA of this
+// one; halfway through a k-step the next k-step's B fragments are read into
+// the other B set.
 template <int G, int P, int TM, int TN>
-__device__ __forceinline__ void body(f32x16 (&acc)[TM / 64][TN / 64], Frag<TM / 64, TN / 64> (&fr)[2],
+__device__ __forceinline__ void body(f32x16 (&acc)[tile_fm(TM, TN)][tile_fn(TM, TN)],
+                                     Frag<tile_fm(TM, TN), tile_fn(TM, TN)>& fr,
                                      const uint16_t* xs, const uint16_t* ws, const Stage<P, TM, TN>& cur,
                                      Stage<P, TM, TN>& nxt, Merged<P, TM, TN>& mg, uint16_t* xs_next,
                                      uint16_t* ws_next, const PrefillArgs& a, int n0, int k_load,
                                      __amdgpu_buffer_rsrc_t xrs, __amdgpu_buffer_rsrc_t prs, uint32_t row_bytes,
                                      int row_a, int row_b, int lane) {
     using St = Stage<P, TM, TN>;
-    constexpr int FM = TM / 64, FN = TN / 64, PER = FM * FN, NM = PER * (kTK / 16);
+    constexpr int FM = St::FM, FN = St::FN, PER = FM * FN, NM = PER * (kTK / 16);
     if constexpr (G < NM) {
         constexpr int kk = G / PER, mi = G % PER, i = mi / FN, j = mi % FN;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kk & 1].a[i], fr[kk & 1].b[j], acc[i][j], 0, 0, 0);
-        if constexpr (mi == PER / 2 && kk + 1 < kTK / 16)
-            read_frags<FM, FN>(fr[(kk + 1) & 1], xs, ws, kk + 1, row_a, row_b, lane);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.a[i], fr.b[kk & 1][j], acc[i][j], 0, 0, 0);
+        if constexpr (kk + 1 < kTK / 16) {
+            if constexpr (j == FN - 1) fr.a[i] = read_a(xs, kk + 1, row_a + 32 * i, lane);
+            if constexpr (mi == PER / 2) {
+#pragma unroll
+                for (int jj = 0; jj < FN; ++jj) fr.b[(kk + 1) & 1][jj] = read_b<TN>(ws, kk + 1, row_b + 32 * jj, lane);
+            }
+        }
         // loads spread over the first half, so the last has half a stage to arrive
         constexpr int NL = St::XI + P, NH = NM / 2;
         if constexpr (G < NH) load_units<P, TM, TN, G * NL / NH, (G + 1) * NL / NH>(nxt, a, n0, k_load, xrs, prs, row_bytes);
@@ -270,24 +300,26 @@ __device__ __forceinline__ void body(f32x16 (&acc)[TM / 64][TN / 64], Frag<TM / 
 }
 
 // The last stage's matrix work alone.
-template <int FM, int FN>
+template <int FM, int FN, int TN>
 __device__ __forceinline__ void mma_stage(f32x16 (&acc)[FM][FN], const uint16_t* xs, const uint16_t* ws,
                                           int row_a, int row_b, int lane) {
 #pragma unroll
     for (int kk = 0; kk < kTK / 16; ++kk) {
         Frag<FM, FN> f;
-        read_frags<FM, FN>(f, xs, ws, kk, row_a, row_b, lane);
+        read_frags<FM, FN, TN>(f, 0, xs, ws, kk, row_a, row_b, lane);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[0][j], acc[i][j], 0, 0, 0);
     }
 }
 
 template <int P, int TM, int TN>
-__global__ __launch_bounds__(kPThreads, (TM * TN > 128 * 128 ? 1 : 2)) void prefill_kernel(PrefillArgs a) {
-    constexpr int FM = TM / 64, FN = TN / 64;
+__global__ __launch_bounds__(64 * tile_waves(TM, TN), (TM * TN > 128 * 128 ? 1 : 2)) void prefill_kernel(
+    PrefillArgs a) {
+    using St = Stage<P, TM, TN>;
+    constexpr int FM = St::FM, FN = St::FN;
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][TM * kTK];
     __shared__ __attribute__((aligned(16))) uint16_t wsh[2][TN * kTK];
     __shared__ float srow[TM];
@@ -296,8 +328,8 @@ __global__ __launch_bounds__(kPThreads, (TM * TN > 128 * 128 ? 1 : 2)) void pref
     const int n0 = (id / a.tiles_m) * TN;
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
-    const int row_a = (wv >> 1) * (TM / 2);     // this wave's first token row in the tile
-    const int row_b = (wv & 1) * (TN / 2);      // and first output
+    const int row_a = (wv / St::WN) * (TM / St::WM);   // this wave's first token row in the tile
+    const int row_b = (wv % St::WN) * (TN / St::WN);   // and first output
     const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint32_t*>(a.planes), static_cast<short>(0), static_cast<int>(a.plane_bytes), 0x00020000);
     const uint32_t row_bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a.row_words) * 4u);
@@ -315,13 +347,12 @@ __global__ __launch_bounds__(kPThreads, (TM * TN > 128 * 128 ? 1 : 2)) void pref
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int n_stages = (a.d_in + kTK - 1) / kTK;
-    using St = Stage<P, TM, TN>;
     // Stage s is computed from LDS while stage s + 1, loaded one iteration
     // earlier, is decoded into the other LDS buffer and stage s + 2 is
     // loaded; stages past the last load nothing (out-of-range offsets).
     St sa, sb;
     Merged<P, TM, TN> mg;
-    Frag<FM, FN> fr[2];
+    Frag<FM, FN> fr;
     load_units<P, TM, TN, 0, St::XI + P>(sa, a, n0, 0, xrs, prs, row_bytes);
     merge_units<P, TM, TN, 0, St::WPT>(sa, mg);
     code_units<P, TM, TN, 0, St::WPT * 2>(mg, wsh[0]);
@@ -330,18 +361,18 @@ __global__ __launch_bounds__(kPThreads, (TM * TN > 128 * 128 ? 1 : 2)) void pref
     __syncthreads();
     int s = 0;
     for (; s + 1 < n_stages; s += 2) {
-        read_frags<FM, FN>(fr[0], xs[0], wsh[0], 0, row_a, row_b, lane);
+        read_frags<FM, FN, TN>(fr, 0, xs[0], wsh[0], 0, row_a, row_b, lane);
         body<0, P, TM, TN>(acc, fr, xs[0], wsh[0], sa, sb, mg, xs[1], wsh[1], a, n0, (s + 2) * kTK, xrs, prs,
                            row_bytes, row_a, row_b, lane);
         __syncthreads();
-        read_frags<FM, FN>(fr[0], xs[1], wsh[1], 0, row_a, row_b, lane);
+        read_frags<FM, FN, TN>(fr, 0, xs[1], wsh[1], 0, row_a, row_b, lane);
         body<0, P, TM, TN>(acc, fr, xs[1], wsh[1], sb, sa, mg, xs[0], wsh[0], a, n0, (s + 3) * kTK, xrs, prs,
                            row_bytes, row_a, row_b, lane);
         __syncthreads();
     }
-    if (s < n_stages) mma_stage<FM, FN>(acc, xs[0], wsh[0], row_a, row_b, lane);
+    if (s < n_stages) mma_stage<FM, FN, TN>(acc, xs[0], wsh[0], row_a, row_b, lane);
 
-    for (int r = threadIdx.x; r < TM; r += kPThreads) {
+    for (int r = threadIdx.x; r < TM; r += St::NT) {
         const int m = m0 + r;
         srow[r] = m < a.M ? a.rowsum[m] : 0.f;
     }
@@ -401,7 +432,7 @@ template <int P, int TM, int TN>
 hipError_t launch_t(PrefillArgs a, hipStream_t stream) {
     a.tiles_m = (a.M + TM - 1) / TM;
     const long tiles = static_cast<long>(a.tiles_m) * ((a.d_out + TN - 1) / TN);
-    prefill_kernel<P, TM, TN><<<dim3(static_cast<unsigned>(tiles)), dim3(kPThreads), 0, stream>>>(a);
+    prefill_kernel<P, TM, TN><<<dim3(static_cast<unsigned>(tiles)), dim3(Stage<P, TM, TN>::NT), 0, stream>>>(a);
     return hipGetLastError();
 }
 
