@@ -80,8 +80,8 @@ int env_int(const char* name);
 // Prefill GEMM: rows sums, then the MFMA kernel (prefill.hip).
 size_t prefill_workspace_bytes(int M);
 long prefill_tiles(const grinqh_layout& L, int M);
-// Tile (tokens x outputs): 256 x 256 when that alone gives every CU a
-// workgroup, else 256 x 128 when that does, else 128 x 128;
+// Tile (tokens x outputs): 256 x 256, 256 x 128 or 128 x 128, whichever has
+// the least estimated time on cu_count CUs (128 x 128 up to 128 tokens);
 // GRINQH_PREFILL_TILE (128, 256 or 2561 for 256 x 128) overrides it.
 hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, const uint32_t* planes,
                           const uint16_t* s, const uint16_t* z, void* y, int y_dtype, float* rowsum,

@@ -72,16 +72,16 @@ __device__ __forceinline__ int tile_off(int r, int c) {
 
 // Element offset of (channel k, output n) in the [64][TN] bf16 code tile: one
 // row per channel (a multiple of 256 bytes), outputs in 16-byte chunks.  With
-// r = k % 4, chunk c sits at c ^ 4r ^ e, e = a + 2 (a ^ bit 3 of c) and
-// a = parity of r ^ (bit 4 of c).  Both access patterns then touch every
-// bank once per 128 bytes: the transposing reads of a 16-lane group (4
-// channels x 16 outputs) and the 16-byte code writes of 8 lanes (2 channels
-// x 4 thread quarters), and likewise per 256 bytes.
+// r = k % 4, chunk c sits at c ^ 4r ^ e, e = (bit 3 of c) + 2 par and par =
+// parity of r ^ (bit 4 of c).  Both access patterns then touch every bank
+// once per 128 bytes: the transposing reads of a 16-lane group (4 channels x
+// 16 outputs) and the 16-byte code writes of 8 lanes (2 channels x 4 thread
+// quarters with four threads per channel, one channel x 8 with eight).
 template <int TN>
 __device__ __forceinline__ int code_off(int k, int n) {
     const int c = n >> 3, r = k & 3;
     const int par = (r ^ (r >> 1) ^ (c >> 4)) & 1;
-    const int e = par | (((par ^ (c >> 3)) & 1) << 1);
+    const int e = ((c >> 3) & 1) | (par << 1);
     return k * TN + ((c ^ (r << 2) ^ e) << 3) + (n & 7);
 }
 
@@ -455,9 +455,12 @@ size_t prefill_workspace_bytes(int M) {
 
 long prefill_tiles(const grinqh_layout& L, int M) { return tiles_of(M, L.d_out, 128, 128); }
 
-// Tiles (tokens x outputs): 256 x 256 once they alone give every CU a
-// workgroup, else 256 x 128 once those do (both one workgroup per CU), else
-// 128 x 128 (two per CU) for small products.
+// Tile shape (tokens x outputs): the least estimated time, counted as the
+// waves of workgroups the CUs run (one 256-token workgroup per CU, two
+// 128 x 128) times the time of one such wave relative to the others (34 : 20
+// : 25 for 256 x 256, 256 x 128 and 128 x 128, and 18 for 128 x 128 tiles
+// that leave each CU at most one, as measured at d_in 4096); up to 128
+// tokens, 128 x 128, since a 256-token tile would be half empty.
 hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, const uint32_t* planes,
                           const uint16_t* s, const uint16_t* z, void* y, int y_dtype, float* rowsum,
                           int cu_count, hipStream_t stream) {
@@ -477,7 +480,13 @@ hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, cons
     a.row_words = L.row_words;
     a.y_dtype = y_dtype;
     a.plane_bytes = static_cast<uint32_t>(static_cast<size_t>(L.d_in) * L.n_planes * L.row_words * 4u);
-    int tile = tiles_of(M, L.d_out, 256, 256) >= cu_count ? 2 : tiles_of(M, L.d_out, 256, 128) >= cu_count ? 1 : 0;
+    const long cus = cu_count > 0 ? cu_count : 1;
+    const long cost256 = 34 * ((tiles_of(M, L.d_out, 256, 256) + cus - 1) / cus);
+    const long cost2561 = 20 * ((tiles_of(M, L.d_out, 256, 128) + cus - 1) / cus);
+    const long t128 = tiles_of(M, L.d_out, 128, 128);
+    const long cost128 = t128 <= cus ? 18 : 25 * ((t128 + 2 * cus - 1) / (2 * cus));
+    int tile = 0;
+    if (M > 128) tile = cost256 <= cost2561 && cost256 <= cost128 ? 2 : cost2561 <= cost128 ? 1 : 0;
     const int env = env_int("GRINQH_PREFILL_TILE");   // 128, 256 (256 x 256) or 2561 (256 x 128)
     if (env == 128 || env == 256 || env == 2561) tile = env == 256 ? 2 : env == 2561 ? 1 : 0;
     switch (L.n_planes) {
