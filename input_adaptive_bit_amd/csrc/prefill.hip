@@ -10,12 +10,12 @@
 // (q <= 255, exact in bf16), so it runs on the bf16 matrix cores with fp32
 // accumulation (v_mfma_f32_32x32x16_bf16); S comes from a row-sum pass.
 //
-// Tiling.  A workgroup computes a TM x TN (tokens x outputs) tile of Y --
-// 256 x 256 or 256 x 128 with eight waves (two per SIMD, so that one wave's
-// waits are covered by the other's matrix work), or 128 x 128 with four
-// waves and two workgroups per CU -- and walks the input channels in stages
-// of 64.  The waves form a grid over the tile, each owning a block of 32 x 32
-// MFMA tiles (128 x 64, 64 x 64 and 64 x 64 tokens x outputs).  Every thread
+// Tiling.  A workgroup of eight waves computes a TM x TN (tokens x outputs)
+// tile of Y -- 256 x 256 or 256 x 128 with one workgroup per CU, 128 x 128
+// with two -- and walks the input channels in stages of 64.  With at least
+// two waves per SIMD, one wave's waits are covered by another's matrix work.
+// The waves form a grid over the tile, each owning a block of 32 x 32 MFMA
+// tiles (128 x 64, 64 x 64 and 32 x 64 tokens x outputs).  Every thread
 // holds, two stages ahead, 16-byte chunks of X and, for one channel, 1, 2 or
 // 4 plane words of consecutive word positions (one load per plane).  While the matrix cores work on stage s, the waves decode
 // stage s + 1 (merge_codes, shared with the decode GEMV, then one byte
@@ -35,12 +35,11 @@ namespace grinqh {
 namespace {
 
 constexpr int kTK = 64;                  // input channels per stage
-// Waves per workgroup: 8 for the 256-token tiles (two per SIMD), else 4.
-// The waves form a WM x WN grid over the tile; the wave grid is 2 x 2 with
-// four waves and (8 / WN) x WN, WN = TN / 64, with eight.
-__host__ __device__ constexpr int tile_waves(int TM, int TN) { return TM == 256 ? 8 : 4; }
-__host__ __device__ constexpr int tile_wn(int TM, int TN) { return tile_waves(TM, TN) == 4 ? 2 : TN / 64; }
-__host__ __device__ constexpr int tile_wm(int TM, int TN) { return tile_waves(TM, TN) / tile_wn(TM, TN); }
+// Eight waves per workgroup, at least two per SIMD, forming a WM x WN grid
+// over the tile with WN = TN / 64: each wave owns TM / WM tokens x 64 outputs.
+constexpr int kPWaves = 8;
+__host__ __device__ constexpr int tile_wn(int TM, int TN) { return TN / 64; }
+__host__ __device__ constexpr int tile_wm(int TM, int TN) { return kPWaves / tile_wn(TM, TN); }
 // 32 x 32 MFMA tiles per wave along the tokens and the outputs
 __host__ __device__ constexpr int tile_fm(int TM, int TN) { return TM / tile_wm(TM, TN) / 32; }
 __host__ __device__ constexpr int tile_fn(int TM, int TN) { return TN / tile_wn(TM, TN) / 32; }
@@ -75,8 +74,8 @@ __device__ __forceinline__ int tile_off(int r, int c) {
 // r = k % 4, chunk c sits at c ^ 4r ^ e, e = (bit 3 of c) + 2 par and par =
 // parity of r ^ (bit 4 of c).  Both access patterns then touch every bank
 // once per 128 bytes: the transposing reads of a 16-lane group (4 channels x
-// 16 outputs) and the 16-byte code writes of 8 lanes (2 channels x 4 thread
-// quarters with four threads per channel, one channel x 8 with eight).
+// 16 outputs) and the 16-byte code writes of 8 lanes (the eight threads of
+// one channel).
 template <int TN>
 __device__ __forceinline__ int code_off(int k, int n) {
     const int c = n >> 3, r = k & 3;
@@ -97,12 +96,13 @@ __device__ __forceinline__ s16x4 read_codes_tr(const uint16_t* ws, int k0, int n
         (__attribute__((address_space(3))) s16x4*)(ws + code_off<TN>(k0 + (i >> 2), n0 + 4 * (i & 3))));
 }
 
-// One stage's operands in flight.  X: chunk item i = t + 256 u is row i / 8,
-// chunk i % 8.  Planes: thread t takes channel k0 + t / 4 and the WPT word
-// positions from (n0 / 16) + (t % 4) WPT, one 4 WPT-byte load per plane.
+// One stage's operands in flight.  X: chunk item i = t + NT u is row i / 8,
+// chunk i % 8.  Planes: with TPC = NT / 64 threads per channel, thread t takes
+// channel k0 + t / TPC and the WPT word positions from
+// (n0 / 16) + (t % TPC) WPT, one 4 WPT-byte load per plane.
 template <int P, int TM, int TN>
 struct Stage {
-    static constexpr int NT = 64 * tile_waves(TM, TN);  // threads
+    static constexpr int NT = 64 * kPWaves;             // threads
     static constexpr int WN = tile_wn(TM, TN), WM = tile_wm(TM, TN);  // wave grid
     static constexpr int FM = tile_fm(TM, TN), FN = tile_fn(TM, TN);
     static constexpr int TPC = NT / kTK;                // threads per input channel
@@ -316,7 +316,7 @@ __device__ __forceinline__ void mma_stage(f32x16 (&acc)[FM][FN], const uint16_t*
 }
 
 template <int P, int TM, int TN>
-__global__ __launch_bounds__(64 * tile_waves(TM, TN), (TM * TN > 128 * 128 ? 1 : 2)) void prefill_kernel(
+__global__ __launch_bounds__(64 * kPWaves, (TM * TN > 128 * 128 ? 1 : 2)) void prefill_kernel(
     PrefillArgs a) {
     using St = Stage<P, TM, TN>;
     constexpr int FM = St::FM, FN = St::FN;
@@ -458,7 +458,7 @@ long prefill_tiles(const grinqh_layout& L, int M) { return tiles_of(M, L.d_out, 
 // Tile shape (tokens x outputs): the least estimated time, counted as the
 // waves of workgroups the CUs run (one 256-token workgroup per CU, two
 // 128 x 128) times the time of one such wave relative to the others (34 : 20
-// : 25 for 256 x 256, 256 x 128 and 128 x 128, and 18 for 128 x 128 tiles
+// : 25 for 256 x 256, 256 x 128 and 128 x 128, and 16 for 128 x 128 tiles
 // that leave each CU at most one, as measured at d_in 4096); up to 128
 // tokens, 128 x 128, since a 256-token tile would be half empty.
 hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, const uint32_t* planes,
@@ -484,7 +484,7 @@ hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, cons
     const long cost256 = 34 * ((tiles_of(M, L.d_out, 256, 256) + cus - 1) / cus);
     const long cost2561 = 20 * ((tiles_of(M, L.d_out, 256, 128) + cus - 1) / cus);
     const long t128 = tiles_of(M, L.d_out, 128, 128);
-    const long cost128 = t128 <= cus ? 18 : 25 * ((t128 + 2 * cus - 1) / (2 * cus));
+    const long cost128 = t128 <= cus ? 16 : 25 * ((t128 + 2 * cus - 1) / (2 * cus));
     int tile = 0;
     if (M > 128) tile = cost256 <= cost2561 && cost256 <= cost128 ? 2 : cost2561 <= cost128 ? 1 : 0;
     const int env = env_int("GRINQH_PREFILL_TILE");   // 128, 256 (256 x 256) or 2561 (256 x 128)
