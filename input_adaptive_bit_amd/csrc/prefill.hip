@@ -17,11 +17,12 @@
 // The waves form a grid over the tile, each owning a block of 32 x 32 MFMA
 // tiles (128 x 64, 64 x 64 and 32 x 64 tokens x outputs).  Every thread
 // holds, two stages ahead, 16-byte chunks of X and, for one channel, 1, 2 or
-// 4 plane words of consecutive word positions (one load per plane).  While the matrix cores work on stage s, the waves decode
-// stage s + 1 (merge_codes, shared with the decode GEMV, then one byte
-// conversion per code, whose fp32 upper half is the code's bf16) into the
-// other half of a double-buffered LDS tile: each MFMA is followed, in a fixed
-// order, by its share of that work and of the loads.
+// 4 plane words of consecutive word positions (one load per plane).  While
+// the matrix cores work on stage s, the waves decode stage s + 1
+// (merge_codes, shared with the decode GEMV, then one byte conversion per
+// code, whose fp32 upper half is the code's bf16) into the other half of a
+// double-buffered LDS tile: each MFMA is followed, in a fixed order, by its
+// share of that work and of the loads.
 //
 // The X tile is [tokens][64 channels] of bf16 (rows of 8 16-byte chunks,
 // permuted by tile_off); the code tile is [64 channels][TN outputs] (chunks
