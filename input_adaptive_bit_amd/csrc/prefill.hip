@@ -58,6 +58,7 @@ struct PrefillArgs {
     const float* rowsum;     // [M]
     void* y;                 // [M][d_out]
     int M, d_in, d_out, row_words, y_dtype, tiles_m;
+    int vec_y;               // y 16-byte aligned and d_out a multiple of 16 bytes' worth of outputs
     uint32_t plane_bytes;
 };
 
@@ -316,6 +317,11 @@ __device__ __forceinline__ void mma_stage(f32x16 (&acc)[FM][FN], const uint16_t*
     }
 }
 
+// One output in fp32, the same operations on either store path.
+__device__ __forceinline__ float y_value(float mul, float acc, float add, float srow) {
+    return __builtin_fmaf(mul, acc, add * srow);
+}
+
 template <int P, int TM, int TN>
 __global__ __launch_bounds__(64 * kPWaves, (TM * TN > 128 * 128 ? 1 : 2)) void prefill_kernel(
     PrefillArgs a) {
@@ -381,6 +387,73 @@ __global__ __launch_bounds__(64 * kPWaves, (TM * TN > 128 * 128 ? 1 : 2)) void p
 
     // y = s_j * u_j * acc + (s_j / 2 + z_j) * S_m, u_j undoing the byte scale
     // of output j's lane in merge_codes (outputs 4b + k sit in byte lane k)
+    if (a.vec_y) {
+        // Through LDS, so that y leaves in 128-byte row segments: each wave
+        // stages its block of y 32 token rows at a time (bf16: 32 x 64; fp32:
+        // 32 x 32 per pass) in the X tile's space, which the barrier above has
+        // freed, and reads it back 16 bytes per lane.
+        static_assert(FN * 32 == 64, "each wave owns 64 outputs");
+        float mul[FN], add[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int nc = min(n0 + row_b + 32 * j + (lane & 31), a.d_out - 1);
+            const float sj = f16_to_f32(a.s[nc]);
+            mul[j] = sj * code_unscale<P>(lane & 3);
+            add[j] = 0.5f * sj + f16_to_f32(a.z[nc]);
+        }
+        const int nb = n0 + row_b;   // the wave's first output
+        if (a.y_dtype == GRINQH_F32) {
+            float* stg = reinterpret_cast<float*>(&xs[0][0]) + wv * 1024;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int mb = row_a + 32 * i;   // the block's first token row in the tile
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        stg[rl * 32 + (lane & 31)] = y_value(mul[j], acc[i][j][r], add[j], srow[mb + rl]);
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {   // rows (lane / 8) + 8q, outputs 4 (lane % 8) .. + 3
+                        const int rl = (lane >> 3) + 8 * q, cl = 4 * (lane & 7), c = 32 * j + cl;
+                        const int m = m0 + mb + rl;
+                        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * 32 + cl);
+                        if (m < a.M && nb + c < a.d_out)
+                            *reinterpret_cast<u32x4*>(static_cast<float*>(a.y) + static_cast<size_t>(m) * a.d_out +
+                                                      nb + c) = v;
+                    }
+                    __syncthreads();
+                }
+        } else {
+            uint16_t* stg = reinterpret_cast<uint16_t*>(&xs[0][0]) + wv * 2048;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int mb = row_a + 32 * i;
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        stg[rl * 64 + 32 * j + (lane & 31)] =
+                            f32_to_bf16_rne(y_value(mul[j], acc[i][j][r], add[j], srow[mb + rl]));
+                    }
+                __syncthreads();
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {   // rows (lane / 8) + 8q, outputs 8 (lane % 8) .. + 7
+                    const int rl = (lane >> 3) + 8 * q, c = 8 * (lane & 7);
+                    const int m = m0 + mb + rl;
+                    const u32x4 w = *reinterpret_cast<const u32x4*>(stg + rl * 64 + c);
+                    if (m < a.M && nb + c < a.d_out)
+                        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.y) + static_cast<size_t>(m) * a.d_out +
+                                                  nb + c) = w;
+                }
+                __syncthreads();
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int n = n0 + row_b + 32 * j + (lane & 31);
@@ -397,7 +470,7 @@ __global__ __launch_bounds__(64 * kPWaves, (TM * TN > 128 * 128 ? 1 : 2)) void p
                 const int ml = row_a + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 const int m = m0 + ml;
                 if (!n_ok || m >= a.M) continue;
-                const float yv = mul * acc[i][j][r] + add * srow[ml];
+                const float yv = y_value(mul, acc[i][j][r], add, srow[ml]);
                 const size_t o = static_cast<size_t>(m) * a.d_out + n;
                 if (a.y_dtype == GRINQH_F32)
                     static_cast<float*>(a.y)[o] = yv;
@@ -480,6 +553,8 @@ hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, cons
     a.d_out = L.d_out;
     a.row_words = L.row_words;
     a.y_dtype = y_dtype;
+    const int y_vec_outputs = y_dtype == GRINQH_F32 ? 4 : 8;   // outputs per 16 bytes
+    a.vec_y = reinterpret_cast<uintptr_t>(y) % 16 == 0 && L.d_out % y_vec_outputs == 0;
     a.plane_bytes = static_cast<uint32_t>(static_cast<size_t>(L.d_in) * L.n_planes * L.row_words * 4u);
     const long cus = cu_count > 0 ? cu_count : 1;
     const long cost256 = 34 * ((tiles_of(M, L.d_out, 256, 256) + cus - 1) / cus);

@@ -73,6 +73,34 @@ def test_prefill_matches_oracle(dev, b_max, M, d_in, d_out):
     assert np.array_equal(got, rne)
 
 
+def test_prefill_output_store_paths_agree(dev):
+    """y leaves through LDS as 16-byte row segments when y is 16-byte aligned
+    and d_out a multiple of 16 bytes' worth of outputs, else element by
+    element; a y view 2 bytes into its buffer takes the second path, and both
+    must give the same bits."""
+    import torch
+    import input_adaptive_bit_amd as G
+    rng = np.random.default_rng(41)
+    M, d_in, d_out = 300, 520, 1024
+    say(f"prefill store paths M={M} {d_in}->{d_out}")
+    q, s, z, X = _inputs(rng, M, d_in, d_out, 8)
+    dl = DeviceLinear(q, s, z, 8, dev)
+    xd, Xh = _x_dev(X, dev)
+    ws = torch.empty(max(G.grinqh_prefill_workspace_bytes(M), 256), dtype=torch.uint8, device=dev)
+    R = O.prefill_gemm(Xh, q, s, z, 8)
+    for dt, tol in ((torch.float32, TOL_F32), (torch.bfloat16, TOL_BF16)):
+        y_vec = torch.empty((M, d_out), dtype=dt, device=dev)
+        buf = torch.empty(M * d_out + 8, dtype=dt, device=dev)
+        y_el = buf[1:1 + M * d_out].view(M, d_out)
+        assert y_vec.data_ptr() % 16 == 0 and y_el.data_ptr() % 16 != 0
+        G.grinqh_prefill_gemm(dl.L, xd, dl.planes, dl.s, dl.z, y_vec, ws)
+        G.grinqh_prefill_gemm(dl.L, xd, dl.planes, dl.s, dl.z, y_el, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y_vec.view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                           y_el.view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+        assert _row_err(y_vec.float().cpu().numpy().astype(np.float64), R) <= tol
+
+
 def test_prefill_integer_case_is_exact(dev):
     """s = 1, z = 0 would leave Y = X (Q + 1/2)^T; with s = 2 and z = -1 every
     weight is the odd integer 2q and Y the integer X (2Q)^T, exactly."""
