@@ -289,12 +289,27 @@ __device__ __forceinline__ void body(f32x16 (&acc)[tile_fm(TM, TN)][tile_fn(TM, 
         // loads spread over the first half, so the last has half a stage to arrive
         constexpr int NL = St::XI + P, NH = NM / 2;
         if constexpr (G < NH) load_units<P, TM, TN, G * NL / NH, (G + 1) * NL / NH>(nxt, a, n0, k_load, xrs, prs, row_bytes);
-        // merges in the first WPT slots, code writes over the rest
-        constexpr int WPT = St::WPT, NU = WPT * 2;
+        // merges in the first WPT slots, code and X writes over the rest but
+        // the last two, which belong to the barrier and the next stage's
+        // first operand reads
+        constexpr int WPT = St::WPT, NU = WPT * 2, NW = NM - 2;
+        static_assert(NW - WPT >= NU && NW >= St::XI, "a write slot for every unit");
         if constexpr (G < WPT) merge_units<P, TM, TN, G, G + 1>(cur, mg);
-        if constexpr (G >= WPT)
-            code_units<P, TM, TN, (G - WPT) * NU / (NM - WPT), (G - WPT + 1) * NU / (NM - WPT)>(mg, ws_next);
-        x_units<P, TM, TN, G * St::XI / NM, (G + 1) * St::XI / NM>(cur, xs_next);
+        if constexpr (G >= WPT && G < NW)
+            code_units<P, TM, TN, (G - WPT) * NU / (NW - WPT), (G - WPT + 1) * NU / (NW - WPT)>(mg, ws_next);
+        if constexpr (G < NW) x_units<P, TM, TN, G * St::XI / NW, (G + 1) * St::XI / NW>(cur, xs_next);
+        // Two MFMAs before the end every read of this stage's tiles has been
+        // consumed and every write of the next stage's has been issued: the
+        // barrier goes here, and the next stage's k-step 0 operands are read
+        // while the last two MFMAs run (A row block FM - 1 after its last use).
+        if constexpr (G == NW) {
+            __syncthreads();
+#pragma unroll
+            for (int ii = 0; ii < FM - 1; ++ii) fr.a[ii] = read_a(xs_next, 0, row_a + 32 * ii, lane);
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj) fr.b[0][jj] = read_b<TN>(ws_next, 0, row_b + 32 * jj, lane);
+        }
+        if constexpr (G == NM - 1) fr.a[FM - 1] = read_a(xs_next, 0, row_a + 32 * (FM - 1), lane);
         __builtin_amdgcn_sched_barrier(0);
         body<G + 1, P, TM, TN>(acc, fr, xs, ws, cur, nxt, mg, xs_next, ws_next, a, n0, k_load, xrs, prs, row_bytes,
                                row_a, row_b, lane);
@@ -366,16 +381,15 @@ __global__ __launch_bounds__(64 * kPWaves, (TM * TN > 128 * 128 ? 1 : 2)) void p
     x_units<P, TM, TN, 0, St::XI>(sa, xs[0]);
     load_units<P, TM, TN, 0, St::XI + P>(sa, a, n0, kTK, xrs, prs, row_bytes);
     __syncthreads();
+    // Each body ends with the barrier and the next stage's k-step 0 operands
+    // in registers; the last one reads a stage past the end (zeros), unused.
+    read_frags<FM, FN, TN>(fr, 0, xs[0], wsh[0], 0, row_a, row_b, lane);
     int s = 0;
     for (; s + 1 < n_stages; s += 2) {
-        read_frags<FM, FN, TN>(fr, 0, xs[0], wsh[0], 0, row_a, row_b, lane);
         body<0, P, TM, TN>(acc, fr, xs[0], wsh[0], sa, sb, mg, xs[1], wsh[1], a, n0, (s + 2) * kTK, xrs, prs,
                            row_bytes, row_a, row_b, lane);
-        __syncthreads();
-        read_frags<FM, FN, TN>(fr, 0, xs[1], wsh[1], 0, row_a, row_b, lane);
         body<0, P, TM, TN>(acc, fr, xs[1], wsh[1], sb, sa, mg, xs[0], wsh[0], a, n0, (s + 3) * kTK, xrs, prs,
                            row_bytes, row_a, row_b, lane);
-        __syncthreads();
     }
     if (s < n_stages) mma_stage<FM, FN, TN>(acc, xs[0], wsh[0], row_a, row_b, lane);
 
