@@ -58,7 +58,8 @@ struct PrefillArgs {
     const float* rowsum;     // [M]
     void* y;                 // [M][d_out]
     int M, d_in, d_out, row_words, y_dtype, tiles_m;
-    int vec_y;               // y 16-byte aligned and d_out a multiple of 16 bytes' worth of outputs
+    int vec_y;
+    int xcd_group;           // tile columns a multiple of 8: map columns to XCDs               // y 16-byte aligned and d_out a multiple of 16 bytes' worth of outputs
     uint32_t plane_bytes;
 };
 
@@ -346,8 +347,20 @@ __global__ __launch_bounds__(64 * kPWaves, (TM * TN > 128 * 128 ? 1 : 2)) void p
     __shared__ __attribute__((aligned(16))) uint16_t wsh[2][TN * kTK];
     __shared__ float srow[TM];
     const int id = static_cast<int>(blockIdx.x);
-    const int m0 = (id % a.tiles_m) * TM;
-    const int n0 = (id / a.tiles_m) * TN;
+    // Workgroups go to the 8 XCDs in turn (id % 8).  When the tile columns
+    // split evenly, XCD x takes the columns x, x + 8, ... whole, so the
+    // workgroups that share an XCD's L2 share plane columns and X rows.
+    int tm, tn;
+    if (a.xcd_group) {
+        const int k = id >> 3;
+        tm = k % a.tiles_m;
+        tn = (id & 7) + 8 * (k / a.tiles_m);
+    } else {
+        tm = id % a.tiles_m;
+        tn = id / a.tiles_m;
+    }
+    const int m0 = tm * TM;
+    const int n0 = tn * TN;
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int row_a = (wv / St::WN) * (TM / St::WM);   // this wave's first token row in the tile
@@ -519,7 +532,9 @@ __global__ __launch_bounds__(256) void rowsum_kernel(const uint16_t* x, int d_in
 template <int P, int TM, int TN>
 hipError_t launch_t(PrefillArgs a, hipStream_t stream) {
     a.tiles_m = (a.M + TM - 1) / TM;
-    const long tiles = static_cast<long>(a.tiles_m) * ((a.d_out + TN - 1) / TN);
+    const int tiles_n = (a.d_out + TN - 1) / TN;
+    a.xcd_group = tiles_n % 8 == 0;
+    const long tiles = static_cast<long>(a.tiles_m) * tiles_n;
     prefill_kernel<P, TM, TN><<<dim3(static_cast<unsigned>(tiles)), dim3(Stage<P, TM, TN>::NT), 0, stream>>>(a);
     return hipGetLastError();
 }
