@@ -296,7 +296,8 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): this decode GEMV is "
-              "built and measured on a single MI355X; see the sharding notes in DESIGN.md.", flush=True)
+              "built and measured on a single MI355X, and how it would shard across GPUs is a design, not code.",
+              flush=True)
         return 2
 
     import torch
