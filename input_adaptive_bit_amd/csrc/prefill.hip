@@ -507,26 +507,27 @@ __global__ __launch_bounds__(64 * kPWaves, (TM * TN > 128 * 128 ? 1 : 2)) void p
     }
 }
 
-// S_m = sum_i X[m][i] in fp32, one workgroup per token row, fixed order.
-__global__ __launch_bounds__(256) void rowsum_kernel(const uint16_t* x, int d_in, float* out) {
-    __shared__ float red[256];
-    const uint16_t* row = x + static_cast<size_t>(blockIdx.x) * d_in;
+// S_m = sum_i X[m][i] in fp32: one wave per token row, in a fixed order
+// (each lane adds its 16-byte chunks lane, lane + 64, ... in turn, then the
+// 64 lane sums are added by xor butterfly, and lane 0's total is stored).
+__global__ __launch_bounds__(256) void rowsum_kernel(const uint16_t* x, int M, int d_in, float* out) {
+    const int row = static_cast<int>(blockIdx.x) * 4 + static_cast<int>(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= M) return;   // whole waves
+    const uint16_t* xr = x + static_cast<size_t>(row) * d_in;
     float acc = 0.f;
-    for (int c = threadIdx.x; c < d_in / 8; c += 256) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(row + 8 * c);
+#pragma unroll 4
+    for (int c = lane; c < d_in / 8; c += 64) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xr + 8 * c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             acc += __uint_as_float(v[e] << 16);
             acc += __uint_as_float(v[e] & 0xFFFF0000u);
         }
     }
-    red[threadIdx.x] = acc;
-    __syncthreads();
-    for (int h = 128; h > 0; h >>= 1) {
-        if (static_cast<int>(threadIdx.x) < h) red[threadIdx.x] += red[threadIdx.x + h];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) out[blockIdx.x] = red[0];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) out[row] = acc;
 }
 
 template <int P, int TM, int TN>
@@ -567,7 +568,7 @@ long prefill_tiles(const grinqh_layout& L, int M) { return tiles_of(M, L.d_out, 
 hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, const uint32_t* planes,
                           const uint16_t* s, const uint16_t* z, void* y, int y_dtype, float* rowsum,
                           int cu_count, hipStream_t stream) {
-    rowsum_kernel<<<dim3(static_cast<unsigned>(M)), dim3(256), 0, stream>>>(x, L.d_in, rowsum);
+    rowsum_kernel<<<dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0, stream>>>(x, M, L.d_in, rowsum);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     PrefillArgs a{};
