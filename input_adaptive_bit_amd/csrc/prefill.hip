@@ -338,6 +338,11 @@ __device__ __forceinline__ float y_value(float mul, float acc, float add, float 
     return __builtin_fmaf(mul, acc, add * srow);
 }
 
+// fp32 -> bf16, round to nearest even (one hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t y_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
 template <int P, int TM, int TN>
 __global__ __launch_bounds__(64 * kPWaves, (TM * TN > 128 * 128 ? 1 : 2)) void prefill_kernel(
     PrefillArgs a) {
@@ -464,7 +469,7 @@ __global__ __launch_bounds__(64 * kPWaves, (TM * TN > 128 * 128 ? 1 : 2)) void p
                     for (int r = 0; r < 16; ++r) {
                         const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                         stg[rl * 64 + 32 * j + (lane & 31)] =
-                            f32_to_bf16_rne(y_value(mul[j], acc[i][j][r], add[j], srow[mb + rl]));
+                            y_bf16(y_value(mul[j], acc[i][j][r], add[j], srow[mb + rl]));
                     }
                 __syncthreads();
 #pragma unroll
@@ -502,7 +507,7 @@ __global__ __launch_bounds__(64 * kPWaves, (TM * TN > 128 * 128 ? 1 : 2)) void p
                 if (a.y_dtype == GRINQH_F32)
                     static_cast<float*>(a.y)[o] = yv;
                 else
-                    static_cast<uint16_t*>(a.y)[o] = f32_to_bf16_rne(yv);
+                    static_cast<uint16_t*>(a.y)[o] = y_bf16(yv);
             }
     }
 }
