@@ -217,20 +217,24 @@ def test_prefill_full_size_sampled(dev, b_max):
 def test_prefill_forced_tiles(dev, monkeypatch, tile, b_max):
     """Every tile shape (128 x 128, 256 x 256 and, as 2561, 256 x 128), forced
     through the library's override, on shapes with ragged token, channel and
-    output tails."""
+    output tails; 300 x 136 -> 2048 has a multiple of 8 tile columns at every
+    tile width (the XCD-grouped tile order) and several tile rows."""
     import torch
     import input_adaptive_bit_amd as G
     monkeypatch.setenv("GRINQH_PREFILL_TILE", str(tile))
-    for M, d_in, d_out in [(300, 4104, 700), (5, 64, 130), (257, 136, 513), (512, 512, 512)]:
+    for M, d_in, d_out in [(300, 4104, 700), (5, 64, 130), (257, 136, 513), (512, 512, 512), (300, 136, 2048)]:
         say(f"prefill forced tile {tile} b_max={b_max} M={M} {d_in}->{d_out}")
         rng = np.random.default_rng(tile + b_max + M + d_in + d_out)
         q, s, z, X = _inputs(rng, M, d_in, d_out, b_max)
         dl = DeviceLinear(q, s, z, b_max, dev)
         xd, Xh = _x_dev(X, dev)
         y = G.prefill_gemm(dl.L, xd, dl.planes, dl.s, dl.z, torch.float32)
+        yb = G.prefill_gemm(dl.L, xd, dl.planes, dl.s, dl.z, torch.bfloat16)
         torch.cuda.synchronize()
-        err = _row_err(y.cpu().numpy().astype(np.float64), O.prefill_gemm(Xh, q, s, z, b_max))
+        R = O.prefill_gemm(Xh, q, s, z, b_max)
+        err = _row_err(y.cpu().numpy().astype(np.float64), R)
         assert err <= TOL_F32, (M, d_in, d_out, err)
+        assert _row_err(yb.float().cpu().numpy().astype(np.float64), R) <= TOL_BF16, (M, d_in, d_out)
 
 
 def test_prefill_maximum_token_count(dev):
