@@ -232,7 +232,10 @@ grinqh_status grinqh_quantize_rtn(int32_t d_in, int32_t d_out, int32_t b_max, co
  *   M          1 .. 2^20 tokens.
  *   planes, s, z  as for grinqh_gemv.
  *   y          [M][d_out] of y_dtype, row-major, overwritten; bf16 output is
- *              the fp32 result rounded to nearest even.
+ *              the fp32 result rounded to nearest even.  A 16-byte aligned y
+ *              with d_out a multiple of 8 (bf16) or 4 (fp32) is written in
+ *              16-byte row segments, otherwise element by element (slower,
+ *              same values).
  *   workspace  >= grinqh_prefill_workspace_bytes(M) bytes (the fp32 row sums
  *              of x), 256-byte aligned, any contents.
  * x and y must not overlap.  The planes must be smaller than 2 GiB. */
