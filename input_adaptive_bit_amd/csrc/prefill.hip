@@ -260,13 +260,13 @@ __device__ __forceinline__ void read_frags(Frag<FM, FN>& f, int set, const uint1
     for (int j = 0; j < FN; ++j) f.b[set][j] = read_b<TN>(ws, kk, row_b + 32 * j, lane);
 }
 
-// Everything a loop body does besides the barrier, as one fixed sequence
-// (scheduling fences between the steps): MFMA G of the current stage, then
-// its share of the loads of the stage after next (over the first half), of the
-// merges and code writes of the next stage and of its X writes.  Each A
-// fragment is reloaded for the next k-step right after its last MFMA of this
-// one; halfway through a k-step the next k-step's B fragments are read into
-// the other B set.
+// One stage as a fixed sequence (scheduling fences between the steps): MFMA
+// G of the current stage, then its share of the loads of the stage after next
+// (over the first half), of the merges and code writes of the next stage and
+// of its X writes.  Each A fragment is reloaded for the next k-step right
+// after its last MFMA of this one; halfway through a k-step the next k-step's
+// B fragments are read into the other B set.  Two MFMAs before the end come
+// the stage barrier and the next stage's k-step 0 operand reads.
 template <int G, int P, int TM, int TN>
 __device__ __forceinline__ void body(f32x16 (&acc)[tile_fm(TM, TN)][tile_fn(TM, TN)],
                                      Frag<tile_fm(TM, TN), tile_fn(TM, TN)>& fr,
