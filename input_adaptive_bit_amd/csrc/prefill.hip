@@ -262,7 +262,7 @@ __device__ __forceinline__ void read_frags(Frag<FM, FN>& f, int set, const uint1
 
 // One stage as a fixed sequence (scheduling fences between the steps): MFMA
 // G of the current stage, then its share of the loads of the stage after next
-// (over the first half), of the merges and code writes of the next stage and
+// (over the first three quarters), of the merges and code writes of the next stage and
 // of its X writes.  Each A fragment is reloaded for the next k-step right
 // after its last MFMA of this one; halfway through a k-step the next k-step's
 // B fragments are read into the other B set.  Two MFMAs before the end come
@@ -287,8 +287,9 @@ __device__ __forceinline__ void body(f32x16 (&acc)[tile_fm(TM, TN)][tile_fn(TM, 
                 for (int jj = 0; jj < FN; ++jj) fr.b[(kk + 1) & 1][jj] = read_b<TN>(ws, kk + 1, row_b + 32 * jj, lane);
             }
         }
-        // loads spread over the first half, so the last has half a stage to arrive
-        constexpr int NL = St::XI + P, NH = NM / 2;
+        // loads spread over the first three quarters of a stage (the first half
+        // at 128 x 128), so the last has a quarter (a half) of one to arrive
+        constexpr int NL = St::XI + P, NH = TM == 256 ? 3 * NM / 4 : NM / 2;
         if constexpr (G < NH) load_units<P, TM, TN, G * NL / NH, (G + 1) * NL / NH>(nxt, a, n0, k_load, xrs, prs, row_bytes);
         // merges in the first WPT slots, code and X writes over the rest but
         // the last two, which belong to the barrier and the next stage's
