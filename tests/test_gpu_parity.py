@@ -505,8 +505,20 @@ def test_gemv_group_matches_oracle_and_single_calls(dev, b_max, x_dtype):
         for k, (o, ref, single) in enumerate(zip(ops, refs, singles)):
             got = o[5].cpu().numpy()
             err = O.max_rel_error(got, ref)
+            sg = single.cpu().numpy()
+            if err > TOL_F32 or O.max_rel_error(got, sg) > 5e-4:
+                # record what a repeat of the launch and of the single call give,
+                # to tell a lasting change of the inputs from a passing one
+                for q in ops:
+                    q[5].fill_(float("nan"))
+                G.grinqh_gemv_group(layouts, ops, ws)
+                again = members[k].gemv(o[0], o[1], torch.float32)
+                torch.cuda.synchronize()
+                say(f"  group member {k} rep {rep}: worst vs oracle {_mismatch(got, ref, 4)}; "
+                    f"vs single {_mismatch(got, sg, 4)}; repeated launch {_mismatch(o[5].cpu().numpy(), ref, 4)}; "
+                    f"repeated single {_mismatch(again.cpu().numpy(), ref, 4)}")
             assert err <= TOL_F32, (rep, k, err, _mismatch(got, ref))
-            assert O.max_rel_error(got, single.cpu().numpy()) <= 5e-4, (rep, k)
+            assert O.max_rel_error(got, sg) <= 5e-4, (rep, k, _mismatch(got, sg))
 
 
 @pytest.mark.parametrize("d_in,d_out,b_max", [(1 << 20, 64, 8), (16, 1 << 20, 4)])
