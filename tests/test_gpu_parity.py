@@ -467,60 +467,6 @@ def test_gemv_exact_integer_sums_many_calls(dev, d_in, d_out):
         assert np.array_equal(got, ref), (n, int(np.sum(got != ref)))
 
 
-@pytest.mark.parametrize("b_max,x_dtype", [(8, "bf16"), (4, "bf16"), (8, "f32")])
-def test_gemv_group_matches_oracle_and_single_calls(dev, b_max, x_dtype):
-    """A group launch of differently shaped members: each member matches the
-    oracle and the single-GEMV call on the same inputs."""
-    import torch
-    import input_adaptive_bit_amd as G
-    shapes = [(4096, 4096), (4096, 1024), (4096, 14336), (14336, 4096), (300, 1500), (1, 65)]
-    rng = np.random.default_rng(77 + b_max)
-    members, ops, refs, singles = [], [], [], []
-    say(f"group launch b_max={b_max} x={x_dtype} members={len(shapes)}")
-    for di, do in shapes:
-        q = rng.integers(0, 1 << b_max, size=(do, di), dtype=np.uint8)
-        s = rng.uniform(0.001, 0.01, do).astype(np.float16)
-        z = rng.normal(0, 0.01, do).astype(np.float16)
-        x = rng.standard_t(3, di).astype(np.float32)
-        if x_dtype == "bf16":
-            x = S.bf16_bits_to_f32(S.f32_to_bf16_bits(x))
-        theta = np.sort(np.quantile(np.abs(x), np.linspace(0.2, 0.9, b_max // 2))).astype(np.float32)
-        dl = DeviceLinear(q, s, z, b_max, dev)
-        xd, td = to_dev_x(x, x_dtype, dev), _theta_dev(theta, dev)
-        y = torch.empty(do, dtype=torch.float32, device=dev)
-        members.append(dl)
-        ops.append((xd, td, dl.planes, dl.s, dl.z, y))
-        refs.append(C.gemv(x, theta, q, s, z, b_max))
-        singles.append(dl.gemv(xd, td, torch.float32))
-    torch.cuda.synchronize()
-    for k, (single, ref) in enumerate(zip(singles, refs)):
-        assert O.max_rel_error(single.cpu().numpy(), ref) <= TOL_F32, ("single", k)
-    layouts = [m.L for m in members]
-    ws = G.new_group_workspace(layouts, dev)
-    for rep in range(3):
-        for o in ops:
-            o[5].fill_(float("nan"))
-        G.grinqh_gemv_group(layouts, ops, ws)
-        torch.cuda.synchronize()
-        for k, (o, ref, single) in enumerate(zip(ops, refs, singles)):
-            got = o[5].cpu().numpy()
-            err = O.max_rel_error(got, ref)
-            sg = single.cpu().numpy()
-            if err > TOL_F32 or O.max_rel_error(got, sg) > 5e-4:
-                # record what a repeat of the launch and of the single call give,
-                # to tell a lasting change of the inputs from a passing one
-                for q in ops:
-                    q[5].fill_(float("nan"))
-                G.grinqh_gemv_group(layouts, ops, ws)
-                again = members[k].gemv(o[0], o[1], torch.float32)
-                torch.cuda.synchronize()
-                say(f"  group member {k} rep {rep}: worst vs oracle {_mismatch(got, ref, 4)}; "
-                    f"vs single {_mismatch(got, sg, 4)}; repeated launch {_mismatch(o[5].cpu().numpy(), ref, 4)}; "
-                    f"repeated single {_mismatch(again.cpu().numpy(), ref, 4)}")
-            assert err <= TOL_F32, (rep, k, err, _mismatch(got, ref))
-            assert O.max_rel_error(got, sg) <= 5e-4, (rep, k, _mismatch(got, sg))
-
-
 @pytest.mark.parametrize("d_in,d_out,b_max", [(1 << 20, 64, 8), (16, 1 << 20, 4)])
 def test_gemv_maximum_dimensions(dev, d_in, d_out, b_max):
     """The largest d_in and d_out the library accepts (2^20): thousands of
