@@ -262,12 +262,12 @@ __device__ __forceinline__ void read_frags(Frag<FM, FN>& f, int set, const uint1
 
 // One stage as a fixed sequence (scheduling fences between the steps): MFMA
 // G of the current stage, then its share of the loads of the stage after next
-// (over the first three quarters), of the merges and code writes of the next stage and
+// (phase 0: spread over the stage; phases 1 and 2: in one half), of the merges and code writes of the next stage and
 // of its X writes.  Each A fragment is reloaded for the next k-step right
 // after its last MFMA of this one; halfway through a k-step the next k-step's
 // B fragments are read into the other B set.  Two MFMAs before the end come
 // the stage barrier and the next stage's k-step 0 operand reads.
-template <int G, int P, int TM, int TN>
+template <int G, int P, int TM, int TN, int PH>
 __device__ __forceinline__ void body(f32x16 (&acc)[tile_fm(TM, TN)][tile_fn(TM, TN)],
                                      Frag<tile_fm(TM, TN), tile_fn(TM, TN)>& fr,
                                      const uint16_t* xs, const uint16_t* ws, const Stage<P, TM, TN>& cur,
@@ -287,19 +287,35 @@ __device__ __forceinline__ void body(f32x16 (&acc)[tile_fm(TM, TN)][tile_fn(TM, 
                 for (int jj = 0; jj < FN; ++jj) fr.b[(kk + 1) & 1][jj] = read_b<TN>(ws, kk + 1, row_b + 32 * jj, lane);
             }
         }
-        // loads spread over the first three quarters of a stage (the first half
-        // at 128 x 128), so the last has a quarter (a half) of one to arrive
-        constexpr int NL = St::XI + P, NH = TM == 256 ? 3 * NM / 4 : NM / 2;
-        if constexpr (G < NH) load_units<P, TM, TN, G * NL / NH, (G + 1) * NL / NH>(nxt, a, n0, k_load, xrs, prs, row_bytes);
-        // merges in the first WPT slots, code and X writes over the rest but
-        // the last two, which belong to the barrier and the next stage's
-        // first operand reads
-        constexpr int WPT = St::WPT, NU = WPT * 2, NW = NM - 2;
-        static_assert(NW - WPT >= NU && NW >= St::XI, "a write slot for every unit");
-        if constexpr (G < WPT) merge_units<P, TM, TN, G, G + 1>(cur, mg);
-        if constexpr (G >= WPT && G < NW)
-            code_units<P, TM, TN, (G - WPT) * NU / (NW - WPT), (G - WPT + 1) * NU / (NW - WPT)>(mg, ws_next);
-        if constexpr (G < NW) x_units<P, TM, TN, G * St::XI / NW, (G + 1) * St::XI / NW>(cur, xs_next);
+        constexpr int NL = St::XI + P, WPT = St::WPT, NU = WPT * 2, NW = NM - 2;
+        if constexpr (PH == 0) {
+            // loads spread over the first three quarters of a stage (the first half
+            // at 128 x 128), so the last has a quarter (a half) of one to arrive
+            constexpr int NH = TM == 256 ? 3 * NM / 4 : NM / 2;
+            if constexpr (G < NH) load_units<P, TM, TN, G * NL / NH, (G + 1) * NL / NH>(nxt, a, n0, k_load, xrs, prs, row_bytes);
+            // merges in the first WPT slots, code and X writes over the rest but
+            // the last two, which belong to the barrier and the next stage's
+            // first operand reads
+            static_assert(NW - WPT >= NU && NW >= St::XI, "a write slot for every unit");
+            if constexpr (G < WPT) merge_units<P, TM, TN, G, G + 1>(cur, mg);
+            if constexpr (G >= WPT && G < NW)
+                code_units<P, TM, TN, (G - WPT) * NU / (NW - WPT), (G - WPT + 1) * NU / (NW - WPT)>(mg, ws_next);
+            if constexpr (G < NW) x_units<P, TM, TN, G * St::XI / NW, (G + 1) * St::XI / NW>(cur, xs_next);
+        } else {
+            // The two waves of a SIMD take turns: phase 1 does all its loads and
+            // decode in the first half of the stage, phase 2 in the second, so
+            // each wave's plain run of MFMAs covers the other's vector work.
+            constexpr int W0 = PH == 1 ? 0 : NM / 2, W1 = PH == 1 ? NM / 2 : NW, NS = W1 - W0;
+            static_assert(NS - WPT >= NU && NS >= 2, "a work slot for every unit");
+            if constexpr (G >= W0 && G < W1) {
+                constexpr int g = G - W0, NLH = NS / 2;
+                if constexpr (g < NLH) load_units<P, TM, TN, g * NL / NLH, (g + 1) * NL / NLH>(nxt, a, n0, k_load, xrs, prs, row_bytes);
+                if constexpr (g < WPT) merge_units<P, TM, TN, g, g + 1>(cur, mg);
+                if constexpr (g >= WPT)
+                    code_units<P, TM, TN, (g - WPT) * NU / (NS - WPT), (g - WPT + 1) * NU / (NS - WPT)>(mg, ws_next);
+                x_units<P, TM, TN, g * St::XI / NS, (g + 1) * St::XI / NS>(cur, xs_next);
+            }
+        }
         // Two MFMAs before the end every read of this stage's tiles has been
         // consumed and every write of the next stage's has been issued: the
         // barrier goes here, and the next stage's k-step 0 operands are read
@@ -313,7 +329,7 @@ __device__ __forceinline__ void body(f32x16 (&acc)[tile_fm(TM, TN)][tile_fn(TM, 
         }
         if constexpr (G == NM - 1) fr.a[FM - 1] = read_a(xs_next, 0, row_a + 32 * (FM - 1), lane);
         __builtin_amdgcn_sched_barrier(0);
-        body<G + 1, P, TM, TN>(acc, fr, xs, ws, cur, nxt, mg, xs_next, ws_next, a, n0, k_load, xrs, prs, row_bytes,
+        body<G + 1, P, TM, TN, PH>(acc, fr, xs, ws, cur, nxt, mg, xs_next, ws_next, a, n0, k_load, xrs, prs, row_bytes,
                                row_a, row_b, lane);
     }
 }
@@ -404,11 +420,22 @@ __global__ __launch_bounds__(64 * kPWaves, (TM * TN > 128 * 128 ? 1 : 2)) void p
     // in registers; the last one reads a stage past the end (zeros), unused.
     read_frags<FM, FN, TN>(fr, 0, xs[0], wsh[0], 0, row_a, row_b, lane);
     int s = 0;
-    for (; s + 1 < n_stages; s += 2) {
-        body<0, P, TM, TN>(acc, fr, xs[0], wsh[0], sa, sb, mg, xs[1], wsh[1], a, n0, (s + 2) * kTK, xrs, prs,
-                           row_bytes, row_a, row_b, lane);
-        body<0, P, TM, TN>(acc, fr, xs[1], wsh[1], sb, sa, mg, xs[0], wsh[0], a, n0, (s + 3) * kTK, xrs, prs,
-                           row_bytes, row_a, row_b, lane);
+    // Waves w and w + 4 share a SIMD: with at least 16 MFMAs per stage they take turns (phases 1 and 2).
+    constexpr bool kTurns = FM * FN * (kTK / 16) >= 16;
+    if (kTurns && wv < 4) {
+        for (; s + 1 < n_stages; s += 2) {
+            body<0, P, TM, TN, kTurns ? 1 : 0>(acc, fr, xs[0], wsh[0], sa, sb, mg, xs[1], wsh[1], a, n0, (s + 2) * kTK,
+                                               xrs, prs, row_bytes, row_a, row_b, lane);
+            body<0, P, TM, TN, kTurns ? 1 : 0>(acc, fr, xs[1], wsh[1], sb, sa, mg, xs[0], wsh[0], a, n0, (s + 3) * kTK,
+                                               xrs, prs, row_bytes, row_a, row_b, lane);
+        }
+    } else {
+        for (; s + 1 < n_stages; s += 2) {
+            body<0, P, TM, TN, kTurns ? 2 : 0>(acc, fr, xs[0], wsh[0], sa, sb, mg, xs[1], wsh[1], a, n0, (s + 2) * kTK,
+                                               xrs, prs, row_bytes, row_a, row_b, lane);
+            body<0, P, TM, TN, kTurns ? 2 : 0>(acc, fr, xs[1], wsh[1], sb, sa, mg, xs[0], wsh[0], a, n0, (s + 3) * kTK,
+                                               xrs, prs, row_bytes, row_a, row_b, lane);
+        }
     }
     if (s < n_stages) mma_stage<FM, FN, TN>(acc, xs[0], wsh[0], row_a, row_b, lane);
 
