@@ -173,6 +173,17 @@ grinqh_status grinqh_gemv_group(const grinqh_layout* layouts, const grinqh_gemv_
 grinqh_status grinqh_debug_codes(const grinqh_layout* L, const uint8_t* bits,
                                  const uint32_t* planes, uint8_t* codes, void* stream);
 
+/* Test and tuning call: force the launch shape of later GEMV and prefill
+ * calls in this process (0 = the library's own choice, the default).
+ *   lane_groups   0, 1, 2, 4 or 8 lane groups per wave: GEMV output tiles of
+ *                 2048, 1024, 512 or 256 outputs.
+ *   chunk         0 or 1 .. 256 input channels per GEMV slice.
+ *   prefill_tile  0, or 1 (128 x 128), 2 (256 x 128), 3 (256 x 256) tokens
+ *                 x outputs per prefill tile.
+ * The GEMV workspace size depends on the shape: query it again after a
+ * change.  EINVAL for any other value (nothing changes).  Host only. */
+grinqh_status grinqh_debug_force_launch(int32_t lane_groups, int32_t chunk, int32_t prefill_tile);
+
 /* ---- Threshold calibration (offline) ----------------------------------
  *
  * KD1 fixes the thresholds offline from the magnitudes of about 128 sample

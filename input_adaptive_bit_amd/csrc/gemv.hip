@@ -39,8 +39,6 @@
 // workgroup, which applies the epilogue y_j = s_j * acc_j + z_j * S (bf16
 // output rounded to nearest even) and clears its workspace row and counter
 // for the next call.
-#include <cstdlib>
-
 #include "decode.hpp"
 #include "internal.h"
 
@@ -109,7 +107,8 @@ struct SliceLists {
     float xv[kMaxChunk];       // x_i * 4^(P - Pi): the multiplier of its Pi-plane code
     uint32_t cnt[4];           // word l, byte w: loaded channels of wave w with l + 1 planes
     float red_s[kWaves], red_c[kWaves];
-    int is_last;
+    int is_last;               // this workgroup arrived last at its tile
+    float S;                   // the tile's sum of x over loaded channels (last arriver)
 };
 
 // Sum over the 64 lanes in a fixed order; every lane gets the total.  Lanes
@@ -359,6 +358,12 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
         s_j[k] = f16_to_f32(D.s[jc]);
         z_j[k] = f16_to_f32(D.z[jc]);
     }
+    // The tile's partial A_j + C_slice and S_slice go to the workspace with
+    // returning agent-scope atomic adds; consuming their results makes the
+    // wave wait until each add has been performed at the device's coherence
+    // point for that address, before the arrival count below is taken.
+    unsigned* ctrl = D.ctrl + static_cast<size_t>(tile) * kCtrlWords;   // own 256-byte line per tile
+    float* ssum = reinterpret_cast<float*>(ctrl + 1);
 #pragma unroll
     for (int k = 0; k < OPT; ++k) {
         const int o = tid + k * kThreads;
@@ -370,37 +375,48 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
         for (int h = NW / 2; h > 0; h /= 2)
 #pragma unroll
             for (int w = 0; w < h; ++w) v[w] += v[w + h];
-        unsafeAtomicAdd(ws_acc + o, v[0] + c_slice);
+        const float old = __hip_atomic_fetch_add(ws_acc + o, v[0] + c_slice, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("" ::"v"(old));
     }
-    unsigned* ctrl = D.ctrl + static_cast<size_t>(tile) * kCtrlWords;   // own 256-byte line per tile
-    float* ssum = reinterpret_cast<float*>(ctrl + 1);
-    if (tid == 0) unsafeAtomicAdd(ssum, s_slice);
+    if (tid == 0) {
+        const float old = __hip_atomic_fetch_add(ssum, s_slice, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("" ::"v"(old));
+    }
 
-    // ---- last workgroup of the tile applies the epilogue.  No device-scope
-    // fence: fp32 atomics are performed at the device coherence point, so each
-    // thread waits until its own atomics have completed (s_waitcnt 0) before the
-    // arrival count is taken, and the elected workgroup reads the row back with
-    // agent-scope loads.  (A __threadfence here writes back and invalidates the
+    // ---- last workgroup of the tile applies the epilogue.  Every thread's
+    // adds are complete (their results were consumed above) before the
+    // barrier, and the arrival count is taken after it, so the workgroup that
+    // sees n_splits - 1 earlier arrivals finds every slice's adds performed.
+    // It takes S and the row back with atomic exchanges against zero (read
+    // and clear in one step at the same coherence point as the adds), after
+    // an agent-scope acquire fence.  S is taken once, by thread 0, and handed
+    // to the other threads through LDS behind a barrier.  (No device-scope
+    // fence on the add side: a __threadfence writes back and invalidates the
     // L2 for every workgroup, which serialises the whole grid.)
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
     if (tid == 0) {
         const unsigned prev = __hip_atomic_fetch_add(ctrl, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        L.is_last = (prev == static_cast<unsigned>(D.n_splits - 1)) ? 1 : 0;
+        const int last = (prev == static_cast<unsigned>(D.n_splits - 1)) ? 1 : 0;
+        L.is_last = last;
+        if (last) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            L.S = __hip_atomic_exchange(ssum, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // every arrival of this call has been counted: reset for the next call
+            __hip_atomic_store(ctrl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     __syncthreads();
     if (!L.is_last) return;
-    const float S = __hip_atomic_load(ssum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const float S = L.S;
     const int j0 = tile * T;
 #pragma unroll
     for (int k = 0; k < OPT; ++k) {
         const int o = tid + k * kThreads;
         const int j = j0 + o;
-        const float a = __hip_atomic_load(ws_acc + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(ws_acc + o, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float a = __hip_atomic_exchange(ws_acc + o, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (j < D.d_out) {
             const float yv = s_j[k] * a + z_j[k] * S;
             if (D.y_dtype == GRINQH_F32)
@@ -408,10 +424,6 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
             else
                 static_cast<uint16_t*>(D.y)[j] = f32_to_bf16_rne(yv);
         }
-    }
-    if (tid == 0) {
-        __hip_atomic_store(ssum, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(ctrl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -435,13 +447,6 @@ hipError_t launch_p(const GemvGroupArgs& a, int G, int total_wg, hipStream_t str
 }  // namespace
 
 int gemv_tile_outputs(int G) { return (kWave / G) * 16 * kV; }
-
-// Optional launch-shape overrides for tuning on new shapes:
-// GRINQH_LANE_GROUPS (1, 2, 4 or 8) and GRINQH_CHUNK (1 .. 256 channels per slice).
-int env_int(const char* name) {
-    const char* v = std::getenv(name);
-    return v ? std::atoi(v) : 0;
-}
 
 GemvPlan plan_gemv(const grinqh_layout& L, const LaunchShape& shape) {
     GemvPlan pl{};
@@ -476,8 +481,10 @@ long launch_workgroups(const grinqh_layout* layouts, int n, int G, int chunk) {
 
 }  // namespace
 
-LaunchShape choose_launch(const grinqh_layout* layouts, int n, const DeviceInfo& dev) {
-    const long cus = dev.cu_count > 0 ? dev.cu_count : 256;
+namespace {
+
+// Launch shape for these GEMVs on a device with `cus` compute units.
+LaunchShape search_launch(const grinqh_layout* layouts, int n, long cus) {
     LaunchShape sh{4, kMaxChunk};
     // Tile width.  Every split of a tile adds one more row of atomics and one
     // more workgroup that the tile's last arriver waits for, and the main
@@ -488,19 +495,67 @@ LaunchShape choose_launch(const grinqh_layout* layouts, int n, const DeviceInfo&
     const long wg4 = launch_workgroups(layouts, n, 4, kMaxChunk);
     if (wg4 > kWgPerCu * cus) sh.lane_groups = 2;
     else if (8 * wg4 < 5 * cus) sh.lane_groups = 8;
-    const int env_groups = env_int("GRINQH_LANE_GROUPS");
-    if (env_groups == 1 || env_groups == 2 || env_groups == 4 || env_groups == 8) sh.lane_groups = env_groups;
     // Slice length.  A launch of W workgroups leaves the CUs unevenly loaded
     // unless W is a multiple of the CU count; shorten the slices (not below
-    // kMinChunk) until W reaches the next multiple, without passing it.
+    // kMinChunk) until W reaches the next multiple, without passing it.  W
+    // does not grow with the slice length, so the shortest slice that stays
+    // within the target is found by bisection.
     const long wmin = launch_workgroups(layouts, n, sh.lane_groups, kMaxChunk);
     const long target = (wmin + cus - 1) / cus * cus;
-    for (int c = kMaxChunk - 1; c >= kMinChunk; --c) {
-        if (launch_workgroups(layouts, n, sh.lane_groups, c) > target) break;
-        sh.chunk = c;
+    int lo = kMinChunk, hi = kMaxChunk;          // W(hi) <= target holds
+    while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (launch_workgroups(layouts, n, sh.lane_groups, mid) <= target) hi = mid;
+        else lo = mid + 1;
     }
-    const int env_chunk = env_int("GRINQH_CHUNK");
-    if (env_chunk >= 1 && env_chunk <= kMaxChunk) sh.chunk = env_chunk;
+    sh.chunk = hi;
+    return sh;
+}
+
+// Launch shapes of recent calls, per host thread: an eager call with the same
+// layouts on the same device pays no search.
+struct PlanCacheEntry {
+    int n, cus, force_groups, force_chunk;
+    int dims[kMaxGroup][3];
+    LaunchShape shape;
+};
+constexpr int kPlanCache = 16;
+thread_local PlanCacheEntry t_plan_cache[kPlanCache];
+thread_local int t_plan_cache_used = 0, t_plan_cache_next = 0;
+
+bool same_key(const PlanCacheEntry& e, const grinqh_layout* layouts, int n, int cus, const LaunchOverride& ov) {
+    if (e.n != n || e.cus != cus || e.force_groups != ov.lane_groups || e.force_chunk != ov.chunk) return false;
+    for (int k = 0; k < n; ++k)
+        if (e.dims[k][0] != layouts[k].d_in || e.dims[k][1] != layouts[k].d_out || e.dims[k][2] != layouts[k].b_max)
+            return false;
+    return true;
+}
+
+}  // namespace
+
+LaunchShape choose_launch(const grinqh_layout* layouts, int n, const DeviceInfo& dev) {
+    const int cus = dev.cu_count > 0 ? dev.cu_count : 256;
+    const LaunchOverride ov = launch_override();
+    for (int k = 0; k < t_plan_cache_used; ++k)
+        if (same_key(t_plan_cache[k], layouts, n, cus, ov)) return t_plan_cache[k].shape;
+    LaunchShape sh = search_launch(layouts, n, cus);
+    if (ov.lane_groups != 0) sh.lane_groups = ov.lane_groups;
+    if (ov.chunk != 0) sh.chunk = ov.chunk;
+    if (n <= kMaxGroup) {
+        PlanCacheEntry& e = t_plan_cache[t_plan_cache_next];
+        t_plan_cache_next = (t_plan_cache_next + 1) % kPlanCache;
+        if (t_plan_cache_used < kPlanCache) ++t_plan_cache_used;
+        e.n = n;
+        e.cus = cus;
+        e.force_groups = ov.lane_groups;
+        e.force_chunk = ov.chunk;
+        for (int k = 0; k < n; ++k) {
+            e.dims[k][0] = layouts[k].d_in;
+            e.dims[k][1] = layouts[k].d_out;
+            e.dims[k][2] = layouts[k].b_max;
+        }
+        e.shape = sh;
+    }
     return sh;
 }
 

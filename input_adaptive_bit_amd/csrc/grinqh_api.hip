@@ -14,6 +14,7 @@ constexpr int kMaxDim = 1 << 20;
 constexpr int kMaxDevices = 64;
 
 std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not queried yet
+std::atomic<int> g_force_groups{0}, g_force_chunk{0}, g_force_prefill{0};
 
 bool valid_layout(const grinqh_layout* L) {
     if (L == nullptr) return false;
@@ -58,6 +59,31 @@ grinqh_status map_error(hipError_t e) {
 }
 
 }  // namespace
+
+grinqh_status map_hip_error(hipError_t e) { return map_error(e); }
+
+grinqh_status check_gemv_operands(const grinqh_layout* L, const void* x, int x_dtype, const float* theta,
+                                  const uint32_t* planes, const uint16_t* s, const uint16_t* z, const void* y,
+                                  int y_dtype) {
+    if (!valid_layout(L) || x == nullptr || theta == nullptr || planes == nullptr || s == nullptr ||
+        z == nullptr || y == nullptr)
+        return GRINQH_EINVAL;
+    if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return GRINQH_EINVAL;
+    if (packed_bytes(L) > kMaxGemvPlaneBytes) return GRINQH_EINVAL;
+    if (!aligned(x, dtype_bytes(x_dtype)) || !aligned(y, dtype_bytes(y_dtype)) || !aligned(theta, 4) ||
+        !aligned(planes, 16) || !aligned(s, 2) || !aligned(z, 2))
+        return GRINQH_EALIGN;
+    // x and y must not overlap
+    if (overlap(x, static_cast<size_t>(L->d_in) * dtype_bytes(x_dtype), y,
+                static_cast<size_t>(L->d_out) * dtype_bytes(y_dtype)))
+        return GRINQH_EINVAL;
+    return GRINQH_OK;
+}
+
+LaunchOverride launch_override() {
+    return LaunchOverride{g_force_groups.load(std::memory_order_relaxed), g_force_chunk.load(std::memory_order_relaxed),
+                          g_force_prefill.load(std::memory_order_relaxed)};
+}
 
 bool current_device_info(DeviceInfo* out, hipError_t* err) {
     int n = 0;
@@ -162,23 +188,10 @@ grinqh_status grinqh_gemv(const grinqh_layout* L, const void* x, grinqh_dtype x_
                           const float* theta, const uint32_t* planes, const uint16_t* s,
                           const uint16_t* z, void* y, grinqh_dtype y_dtype, void* workspace,
                           size_t workspace_bytes, void* stream) {
-    if (!valid_layout(L) || x == nullptr || theta == nullptr || planes == nullptr ||
-        s == nullptr || z == nullptr || y == nullptr || workspace == nullptr)
-        return GRINQH_EINVAL;
-    if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return GRINQH_EINVAL;
-    if (packed_bytes(L) > kMaxGemvPlaneBytes) return GRINQH_EINVAL;
-    if (!aligned(x, dtype_bytes(x_dtype)) || !aligned(y, dtype_bytes(y_dtype)) ||
-        !aligned(theta, 4) || !aligned(planes, 16) || !aligned(s, 2) || !aligned(z, 2) ||
-        !aligned(workspace, 256))
-        return GRINQH_EALIGN;
-    {
-        // x and y must not overlap
-        uintptr_t xb = reinterpret_cast<uintptr_t>(x);
-        uintptr_t xe = xb + static_cast<size_t>(L->d_in) * dtype_bytes(x_dtype);
-        uintptr_t yb = reinterpret_cast<uintptr_t>(y);
-        uintptr_t ye = yb + static_cast<size_t>(L->d_out) * dtype_bytes(y_dtype);
-        if (xb < ye && yb < xe) return GRINQH_EINVAL;
-    }
+    const grinqh_status st = check_gemv_operands(L, x, x_dtype, theta, planes, s, z, y, y_dtype);
+    if (st != GRINQH_OK) return st;
+    if (workspace == nullptr) return GRINQH_EINVAL;
+    if (!aligned(workspace, 256)) return GRINQH_EALIGN;
     DeviceInfo dev;
     hipError_t e;
     if (!current_device_info(&dev, &e)) return map_error(e);
@@ -271,6 +284,16 @@ grinqh_status grinqh_prefill_gemm(const grinqh_layout* L, const void* x, grinqh_
     if (!current_device_info(&dev, &e)) return map_error(e);
     return map_error(launch_prefill(*L, static_cast<const uint16_t*>(x), M, planes, s, z, y, y_dtype,
                                     static_cast<float*>(workspace), dev.cu_count, static_cast<hipStream_t>(stream)));
+}
+
+grinqh_status grinqh_debug_force_launch(int32_t lane_groups, int32_t chunk, int32_t prefill_tile) {
+    if (lane_groups != 0 && lane_groups != 1 && lane_groups != 2 && lane_groups != 4 && lane_groups != 8)
+        return GRINQH_EINVAL;
+    if (chunk < 0 || chunk > 256 || prefill_tile < 0 || prefill_tile > 3) return GRINQH_EINVAL;
+    g_force_groups.store(lane_groups, std::memory_order_relaxed);
+    g_force_chunk.store(chunk, std::memory_order_relaxed);
+    g_force_prefill.store(prefill_tile, std::memory_order_relaxed);
+    return GRINQH_OK;
 }
 
 grinqh_status grinqh_debug_codes(const grinqh_layout* L, const uint8_t* bits,

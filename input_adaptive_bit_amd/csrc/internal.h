@@ -17,6 +17,15 @@ struct DeviceInfo {
 // Cached per-device query; false if no device is visible or the query failed.
 bool current_device_info(DeviceInfo* out, hipError_t* err);
 
+// Status code of a HIP error.
+grinqh_status map_hip_error(hipError_t e);
+
+// Host checks of grinqh_gemv's operands (all but the workspace): GRINQH_OK,
+// or the status the call returns without touching the device.
+grinqh_status check_gemv_operands(const grinqh_layout* L, const void* x, int x_dtype, const float* theta,
+                                  const uint32_t* planes, const uint16_t* s, const uint16_t* z, const void* y,
+                                  int y_dtype);
+
 hipError_t launch_pack(const grinqh_layout& L, const uint8_t* q, uint32_t* planes,
                        hipStream_t stream);
 
@@ -67,22 +76,28 @@ struct LaunchShape {
 
 // Plan of one GEMV at a launch shape.
 GemvPlan plan_gemv(const grinqh_layout& L, const LaunchShape& shape);
+// Process-wide launch-shape overrides set through grinqh_debug_force_launch
+// (0 = the library's own choice).
+struct LaunchOverride {
+    int lane_groups;    // 0, 1, 2, 4 or 8
+    int chunk;          // 0 or 1 .. 256
+    int prefill_tile;   // 0, 1 (128 x 128), 2 (256 x 128) or 3 (256 x 256)
+};
+LaunchOverride launch_override();
+
 // Launch shape for one launch of these n GEMVs (a group, or n = 1): slices
 // of up to 256 channels, 4 lane groups per wave (2 when that gives more than
 // four workgroups per CU, 8 when it gives too few to reach most CUs), and
 // the slices shortened until the workgroup count reaches a multiple of the
-// CU count.  GRINQH_LANE_GROUPS and GRINQH_CHUNK override it.
+// CU count; then the overrides.  Cached per host thread.
 LaunchShape choose_launch(const grinqh_layout* layouts, int n, const DeviceInfo& dev);
-
-// Integer value of an environment variable (0 if unset).
-int env_int(const char* name);
 
 // Prefill GEMM: rows sums, then the MFMA kernel (prefill.hip).
 size_t prefill_workspace_bytes(int M);
 long prefill_tiles(const grinqh_layout& L, int M);
 // Tile (tokens x outputs): 256 x 256, 256 x 128 or 128 x 128, whichever has
-// the least estimated time on cu_count CUs (128 x 128 up to 128 tokens);
-// GRINQH_PREFILL_TILE (128, 256 or 2561 for 256 x 128) overrides it.
+// the least estimated time on cu_count CUs (128 x 128 up to 128 tokens),
+// unless an override is set.
 hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, const uint32_t* planes,
                           const uint16_t* s, const uint16_t* z, void* y, int y_dtype, float* rowsum,
                           int cu_count, hipStream_t stream);

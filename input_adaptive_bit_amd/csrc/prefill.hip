@@ -626,8 +626,8 @@ hipError_t launch_prefill(const grinqh_layout& L, const uint16_t* x, int M, cons
     const long cost128 = t128 <= cus ? 16 : 25 * ((t128 + 2 * cus - 1) / (2 * cus));
     int tile = 0;
     if (M > 128) tile = cost256 <= cost2561 && cost256 <= cost128 ? 2 : cost2561 <= cost128 ? 1 : 0;
-    const int env = env_int("GRINQH_PREFILL_TILE");   // 128, 256 (256 x 256) or 2561 (256 x 128)
-    if (env == 128 || env == 256 || env == 2561) tile = env == 256 ? 2 : env == 2561 ? 1 : 0;
+    const int forced = launch_override().prefill_tile;   // 1: 128 x 128, 2: 256 x 128, 3: 256 x 256
+    if (forced != 0) tile = forced - 1;
     switch (L.n_planes) {
         case 1: return launch_p<1>(a, tile, stream);
         case 2: return launch_p<2>(a, tile, stream);

@@ -46,6 +46,7 @@ MAX_GROUP = 8
 EXPORTS = ("grinqh_version", "grinqh_status_string", "grinqh_layout_init", "grinqh_packed_bytes",
            "grinqh_gemv_workspace_bytes", "grinqh_pack", "grinqh_assign_bits", "grinqh_gemv",
            "grinqh_gemv_group_workspace_bytes", "grinqh_gemv_group", "grinqh_debug_codes",
+           "grinqh_debug_force_launch",
            "grinqh_calibrate_workspace_bytes", "grinqh_calibrate_thresholds", "grinqh_quantize_rtn",
            "grinqh_prefill_workspace_bytes", "grinqh_prefill_gemm")
 
@@ -93,6 +94,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.grinqh_gemv_group.restype = ctypes.c_int
     lib.grinqh_debug_codes.argtypes = [LP, vp, vp, vp, vp]
     lib.grinqh_debug_codes.restype = ctypes.c_int
+    lib.grinqh_debug_force_launch.argtypes = [i32, i32, i32]
+    lib.grinqh_debug_force_launch.restype = ctypes.c_int
     lib.grinqh_calibrate_workspace_bytes.argtypes = []
     lib.grinqh_calibrate_workspace_bytes.restype = sz
     lib.grinqh_calibrate_thresholds.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_double),
@@ -248,6 +251,20 @@ def grinqh_debug_codes(L: Layout, bits, planes, codes, stream=None) -> None:
     _check(load().grinqh_debug_codes(ctypes.byref(L), _ptr(bits), _ptr(planes), _ptr(codes),
                                      _stream(stream)),
            "grinqh_debug_codes")
+
+
+def grinqh_debug_force_launch(lane_groups: int, chunk: int, prefill_tile: int) -> None:
+    _check(load().grinqh_debug_force_launch(int(lane_groups), int(chunk), int(prefill_tile)),
+           "grinqh_debug_force_launch")
+
+
+_PREFILL_TILE_CODES = {0: 0, (128, 128): 1, (256, 128): 2, (256, 256): 3}
+
+
+def force_launch_shape(lane_groups: int = 0, chunk: int = 0, prefill_tile=0) -> None:
+    """Force the GEMV tile width (lane groups per wave), slice length and the
+    prefill tile ((tokens, outputs) or 0) of later calls; 0 = automatic."""
+    grinqh_debug_force_launch(lane_groups, chunk, _PREFILL_TILE_CODES[prefill_tile])
 
 
 def grinqh_calibrate_workspace_bytes() -> int:

@@ -242,3 +242,14 @@ def test_prefill_argument_checks_before_any_device_call():
     assert call(y=X + 64) == B.GRINQH_EINVAL                # y overlaps x
     big = G.grinqh_layout_init(1 << 20, 4096, 8)           # 4 GiB of planes
     assert call(L=ctypes.byref(big), M=1, b=1 << 30) == B.GRINQH_EINVAL
+
+
+def test_force_launch_argument_checks():
+    """The test override of the launch shape rejects values outside its
+    documented sets, and accepts (then clears) valid ones; host only."""
+    import input_adaptive_bit_amd as B
+    lib = B.load()
+    for bad in [(3, 0, 0), (16, 0, 0), (-1, 0, 0), (0, -1, 0), (0, 257, 0), (0, 0, 4), (0, 0, -1)]:
+        assert lib.grinqh_debug_force_launch(*bad) == 1, bad   # GRINQH_EINVAL
+    for good in [(1, 7, 1), (8, 256, 3), (2, 64, 2), (0, 0, 0)]:
+        assert lib.grinqh_debug_force_launch(*good) == 0, good   # GRINQH_OK

@@ -27,6 +27,14 @@ def dev():
     return require_gpu()
 
 
+@pytest.fixture
+def forced_shape():
+    """Force a GEMV launch shape for one test; back to automatic afterwards."""
+    import input_adaptive_bit_amd as G
+    yield G.force_launch_shape
+    G.force_launch_shape(0, 0)
+
+
 def _theta_dev(theta, dev):
     return to_dev(np.asarray(theta, np.float32), dev)
 
@@ -187,16 +195,15 @@ def test_gemv_ragged_shapes(dev, b_max, d_in, d_out, x_dtype):
 @pytest.mark.parametrize("lane_groups", [1, 2, 4, 8])
 @pytest.mark.parametrize("chunk", [7, 64, 256])
 @pytest.mark.parametrize("b_max", [8, 4])
-def test_gemv_forced_launch_shapes(dev, monkeypatch, lane_groups, chunk, b_max):
+def test_gemv_forced_launch_shapes(dev, forced_shape, lane_groups, chunk, b_max):
     """Every tile width (1, 2, 4 or 8 lane groups per wave) with a short, a
-    mid and the longest slice length, forced through the library's tuning
-    overrides, on shapes with several tiles and slices and ragged tails and on
+    mid and the longest slice length, forced through the library's test
+    override (grinqh_debug_force_launch), on shapes with several tiles and slices and ragged tails and on
     a one-channel layout narrower than one tile: single calls and a group call
     against the oracle."""
     import torch
     import input_adaptive_bit_amd as G
-    monkeypatch.setenv("GRINQH_LANE_GROUPS", str(lane_groups))
-    monkeypatch.setenv("GRINQH_CHUNK", str(chunk))
+    forced_shape(lane_groups, chunk)
     rng = np.random.default_rng(lane_groups * 1000 + chunk + b_max)
     members, ops, refs = [], [], []
     for d_in, d_out in [(1500, 2500), (513, 4100), (40, 70), (1, 65)]:
@@ -310,7 +317,11 @@ def test_gemv_bruteforce_8x8(dev):
     assert worst <= TOL_F32
 
 
-def test_gemv_power_of_two_scaling_is_exact(dev):
+def test_gemv_power_of_two_scaling_general_inputs(dev):
+    """Heavy-tailed x: scaling x and theta by 2^m keeps b and the codes and
+    scales y by 2^m up to the fp32 rounding of the slice sums, whose order
+    between calls is not fixed (exact scaling, with exact sums, is checked in
+    test_gpu_reduction)."""
     import torch
     rng = np.random.default_rng(9)
     d_in, d_out = 1500, 2100

@@ -212,19 +212,28 @@ def test_prefill_full_size_sampled(dev, b_max):
     assert err <= TOL_BF16
 
 
-@pytest.mark.parametrize("tile", [128, 256, 2561])
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256), (256, 128)])
 @pytest.mark.parametrize("b_max", [2, 8])
-def test_prefill_forced_tiles(dev, monkeypatch, tile, b_max):
-    """Every tile shape (128 x 128, 256 x 256 and, as 2561, 256 x 128), forced
-    through the library's override, on shapes with ragged token, channel and
+def test_prefill_forced_tiles(dev, tile, b_max):
+    """Every tile shape (128 x 128, 256 x 256 and 256 x 128 tokens x outputs),
+    forced through the library's test override (grinqh_debug_force_launch), on shapes with ragged token, channel and
     output tails; 300 x 136 -> 2048 has a multiple of 8 tile columns at every
     tile width (the XCD-grouped tile order) and several tile rows."""
     import torch
     import input_adaptive_bit_amd as G
-    monkeypatch.setenv("GRINQH_PREFILL_TILE", str(tile))
+    G.force_launch_shape(0, 0, tile)
+    try:
+        _forced_tile_cases(dev, tile, b_max)
+    finally:
+        G.force_launch_shape(0, 0, 0)
+
+
+def _forced_tile_cases(dev, tile, b_max):
+    import torch
+    import input_adaptive_bit_amd as G
     for M, d_in, d_out in [(300, 4104, 700), (5, 64, 130), (257, 136, 513), (512, 512, 512), (300, 136, 2048)]:
         say(f"prefill forced tile {tile} b_max={b_max} M={M} {d_in}->{d_out}")
-        rng = np.random.default_rng(tile + b_max + M + d_in + d_out)
+        rng = np.random.default_rng(tile[0] + tile[1] // 128 + b_max + M + d_in + d_out)
         q, s, z, X = _inputs(rng, M, d_in, d_out, b_max)
         dl = DeviceLinear(q, s, z, b_max, dev)
         xd, Xh = _x_dev(X, dev)
