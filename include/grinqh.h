@@ -133,6 +133,26 @@ grinqh_status grinqh_gemv(const grinqh_layout* L, const void* x, grinqh_dtype x_
                           const uint16_t* z, void* y, grinqh_dtype y_dtype, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* grinqh_gemv without a workspace argument, for callers that cannot allocate
+ * device memory: code under stream capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments (minus the workspace), checks,
+ * kernels and results as grinqh_gemv.  The workspace is a static device
+ * array of GRINQH_NOALLOC_SCRATCH_BYTES inside the library: every GPU the
+ * library runs on holds its own copy until the process ends, and the call
+ * allocates nothing.  The first call on a device also queues a kernel that
+ * clears that device's copy, ahead of the GEMV on the same stream; every
+ * call leaves it cleared for the next one.
+ *   Returns ENOSPACE when this layout needs more workspace than the array
+ *   holds (grinqh_gemv_workspace_bytes(L) > GRINQH_NOALLOC_SCRATCH_BYTES;
+ *   about 230 thousand outputs), ENODEV beyond 64 devices.
+ * All calls on one GPU share its array: calls that can overlap in time on
+ * one GPU (other streams, other host threads) race and give wrong results;
+ * order them on one stream. */
+#define GRINQH_NOALLOC_SCRATCH_BYTES (1u << 20)
+grinqh_status grinqh_gemv_noalloc(const grinqh_layout* L, const void* x, grinqh_dtype x_dtype,
+                                  const float* theta, const uint32_t* planes, const uint16_t* s,
+                                  const uint16_t* z, void* y, grinqh_dtype y_dtype, void* stream);
+
 /* Operands of one GEMV in a group call (all device pointers, same meaning and
  * alignment as the grinqh_gemv arguments of the same names). */
 typedef struct {

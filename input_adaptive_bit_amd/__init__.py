@@ -9,7 +9,7 @@ from .grinqh import (  # noqa: F401
     GRINQH_BF16, GRINQH_F32, GrinqhError, Layout, EXPORTS, load, status_string,
     grinqh_layout_init, grinqh_packed_bytes, grinqh_gemv_workspace_bytes,
     grinqh_pack, grinqh_assign_bits, grinqh_gemv, grinqh_debug_codes,
-    grinqh_debug_force_launch, force_launch_shape,
+    grinqh_debug_force_launch, force_launch_shape, grinqh_gemv_noalloc, NOALLOC_SCRATCH_BYTES,
     grinqh_gemv_group_workspace_bytes, grinqh_gemv_group, Operands, MAX_GROUP,
     new_workspace, new_group_workspace, pack, assign_bits, gemv, debug_codes,
     grinqh_calibrate_workspace_bytes, grinqh_calibrate_thresholds, calibrate_thresholds,

@@ -46,7 +46,7 @@ MAX_GROUP = 8
 EXPORTS = ("grinqh_version", "grinqh_status_string", "grinqh_layout_init", "grinqh_packed_bytes",
            "grinqh_gemv_workspace_bytes", "grinqh_pack", "grinqh_assign_bits", "grinqh_gemv",
            "grinqh_gemv_group_workspace_bytes", "grinqh_gemv_group", "grinqh_debug_codes",
-           "grinqh_debug_force_launch",
+           "grinqh_debug_force_launch", "grinqh_gemv_noalloc",
            "grinqh_calibrate_workspace_bytes", "grinqh_calibrate_thresholds", "grinqh_quantize_rtn",
            "grinqh_prefill_workspace_bytes", "grinqh_prefill_gemm")
 
@@ -94,6 +94,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.grinqh_gemv_group.restype = ctypes.c_int
     lib.grinqh_debug_codes.argtypes = [LP, vp, vp, vp, vp]
     lib.grinqh_debug_codes.restype = ctypes.c_int
+    lib.grinqh_gemv_noalloc.argtypes = [LP, vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int, vp]
+    lib.grinqh_gemv_noalloc.restype = ctypes.c_int
     lib.grinqh_debug_force_launch.argtypes = [i32, i32, i32]
     lib.grinqh_debug_force_launch.restype = ctypes.c_int
     lib.grinqh_calibrate_workspace_bytes.argtypes = []
@@ -211,6 +213,24 @@ def grinqh_gemv(L: Layout, x, theta, planes, s, z, y, workspace, stream=None) ->
                               _ptr(s), _ptr(z), _ptr(y), _dtype_code(y), _ptr(workspace), ws_bytes,
                               _stream(stream)),
            "grinqh_gemv")
+
+
+NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def grinqh_gemv_noalloc(L: Layout, x, theta, planes, s, z, y, stream=None) -> None:
+    """grinqh_gemv with the library's static device workspace (no workspace
+    argument; the call allocates nothing)."""
+    import torch
+    _need(x, "x", (torch.bfloat16, torch.float32), L.d_in * x.element_size())
+    _need(theta, "theta", (torch.float32,), 4 * L.n_planes)
+    _need(planes, "planes", (torch.int32, torch.uint32), grinqh_packed_bytes(L))
+    _need(s, "s", (torch.float16,), 2 * L.d_out)
+    _need(z, "z", (torch.float16,), 2 * L.d_out)
+    _need(y, "y", (torch.bfloat16, torch.float32), L.d_out * y.element_size())
+    _check(load().grinqh_gemv_noalloc(ctypes.byref(L), _ptr(x), _dtype_code(x), _ptr(theta), _ptr(planes),
+                                      _ptr(s), _ptr(z), _ptr(y), _dtype_code(y), _stream(stream)),
+           "grinqh_gemv_noalloc")
 
 
 def grinqh_gemv_group_workspace_bytes(layouts) -> int:

@@ -112,6 +112,20 @@ def test_argument_checks_before_any_device_call():
     assert G.grinqh_packed_bytes(big) == 1 << 31
     assert lib.grinqh_gemv(ctypes.byref(big), X, 0, TH, PL, S, Z, Y, 1, WS, 1 << 40, None) == B.GRINQH_EINVAL
 
+    # the no-allocation variant runs the same operand checks
+    def noalloc(a):
+        return lib.grinqh_gemv_noalloc(Lp, a["x"], a["xd"], a["th"], a["pl"], a["s"], a["z"], a["y"], a["yd"],
+                                       None)
+
+    for key in ("x", "th", "pl", "s", "z", "y"):
+        assert noalloc(ok(**{key: None})) == B.GRINQH_EINVAL, key
+    assert noalloc(ok(xd=7)) == B.GRINQH_EINVAL
+    assert noalloc(ok(pl=PL + 4)) == B.GRINQH_EALIGN
+    assert noalloc(ok(y=Y + 2)) == B.GRINQH_EALIGN
+    assert noalloc(ok(y=X + 128)) == B.GRINQH_EINVAL
+    assert lib.grinqh_gemv_noalloc(None, X, 0, TH, PL, S, Z, Y, 1, None) == B.GRINQH_EINVAL
+    assert lib.grinqh_gemv_noalloc(ctypes.byref(big), X, 0, TH, PL, S, Z, Y, 1, None) == B.GRINQH_EINVAL
+
     assert lib.grinqh_pack(Lp, None, PL, None) == B.GRINQH_EINVAL
     assert lib.grinqh_pack(Lp, X, None, None) == B.GRINQH_EINVAL
     assert lib.grinqh_pack(Lp, X, PL + 8, None) == B.GRINQH_EALIGN
