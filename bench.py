@@ -3,27 +3,33 @@
 
 One step = the three 8B-shaped decode linears (4096->4096, 4096->14336,
 14336->4096; b_max 8; bf16 x ~ Student-t(3); per-output fp16 s, z; bf16 y)
-at about 3 effective bits, computed by one grinqh_gemv_group call (bit
-assignment, prefix-plane streaming, midpoint dequant and the product for all
-three, in one launch of the HIP library's GEMV kernel).  Inputs are resident in HBM before timing starts.  The steps rotate
-over enough packed weight copies (>= 512 MB) that the 256 MB Infinity Cache
-cannot hold them.  The timed region is one HIP graph holding exactly K steps,
+at about 3 effective bits, as three grinqh_gemv calls one after another (the
+order a decoder runs them in: each call is its own kernel launch doing bit
+assignment, prefix-plane streaming, midpoint dequant and the product).
+Inputs are resident in HBM before timing starts.  The steps rotate over
+enough packed weight copies (>= 512 MB) that the 256 MB Infinity Cache cannot
+hold them.  The timed region is one HIP graph holding exactly K steps,
 bracketed by device synchronisation and HIP events on the launch stream.
 
 Reported value: required bytes per second, where required bytes = taken
 2-bit planes (sum_i b_i * d_out / 8) + fp16 s and z (4 * d_out), summed over
-the step's GEMVs.  Also reported: the effective-bits sweep 2/3/4/8 (8 = all
-channels at b_max, the dense dequant GEMV of the same kernel), the same step
-stored at b_max 6 (levels 0/2/4/6) at 2/3/4/6 effective bits, the whole
-32-layer decode step (128 launches in dependency order: per layer the fused
-q|k|v, o, fused gate|up and down projections; 7.0 GB of planes at b_max 8) at
-the same effective bits, the offline threshold calibration (exact quantiles of
-128 samples' |x|) and RTN quantisation (bf16 weights to b_max 8 codes), the
-prefill-stage dense b_max GEMM on the matrix cores (2048 tokens through a
-4096->16384 up projection at b_max 8 and 4, and through 4096->4096; TFLOP/s
-against the bf16 matrix peak, with torch's bf16 matmul of a dense weight of the
-same shape beside it), and the plain fp64 C oracle timed on the host cores over
-a bounded sample.
+the step's GEMVs.  Also reported, each GEMV in its own launch unless stated:
+ * b_max 8 sweep over 2/3/4/8 effective bits (8 = every channel at b_max: the
+   dense dequant GEMV of the same kernel), the same three linears as one
+   grinqh_gemv_group launch, and a straight-line fit of latency against
+   effective bits per linear (intercept = the fixed cost of a launch);
+ * b_max 4 (levels 0/2/4) at 1.5/2/3/4 effective bits, 4 being its dense mode;
+ * b_max 6 (levels 0/2/4/6) at 2/3/4/6;
+ * the 70B shapes (8192->8192, 8192->28672, 28672->8192) at 2 and 3 bits,
+   rotating over 8 weight copies (4.3 GB of planes);
+ * the whole 32-layer 8B decode step (128 launches in dependency order: per
+   layer fused q|k|v, o, fused gate|up, down; 7.0 GB of planes at b_max 8) at
+   2/3/4/6/8 bits, with its fit;
+ * the offline threshold calibration and RTN quantisation, and the prefill
+   dense b_max GEMM on the matrix cores (TFLOP/s against the bf16 peak, with
+   torch's bf16 matmul of a dense weight of the same shape beside it);
+ * the plain fp64 C oracle timed on the host, on one thread and on every
+   core, over a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -62,43 +68,66 @@ def required_bytes(bits_np: np.ndarray, d_out: int) -> float:
     return float(bits_np.astype(np.int64).sum()) * d_out / 8.0 + 4.0 * d_out
 
 
-def counted_traffic(eff: int):
-    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary
-    (scaled by a copy kernel of known size), or None when that summary was
-    taken on other kernel sources or another workload."""
+def kernel_sources_hash() -> str:
     import hashlib
-    if eff != 3:
-        return None
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic(eff: int):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary
+    (scaled by a copy kernel of known size), or None when that summary was
+    taken on other kernel sources or another workload."""
+    if eff != 3:
+        return None
     try:
         with open(os.path.join(ROOT, COUNTER_SUMMARY)) as fh:
             text = fh.read()
     except OSError:
         return None
     fields = dict(line.split(": ", 1) for line in text.splitlines() if line.startswith(("traffic_", "kernel_")))
-    if fields.get("kernel_sources_sha256", "").strip() != h.hexdigest():
+    if fields.get("kernel_sources_sha256", "").strip() != kernel_sources_hash():
+        return None
+    if fields.get("traffic_workload", "").strip() != "per-call":
         return None
     return int(float(fields["traffic_bytes_per_launch"]))
 
 
+def fit_line(xs, ys):
+    """Least-squares y = a + b x: (a, b)."""
+    x = np.asarray(xs, np.float64)
+    y = np.asarray(ys, np.float64)
+    b, a = np.polyfit(x, y, 1)
+    return float(a), float(b)
+
+
 class Shape:
-    def __init__(self, spec, n_copies, dev, effs):
+    """One linear on the device: n_copies packed code copies (copy 0 from the
+    numpy generator, the rest drawn on the device), s, z, x, and a threshold
+    vector per effective-bits target (same codes, scales and x for all)."""
+
+    def __init__(self, spec, n_copies, dev, effs, host_codes=True):
         import torch
         import input_adaptive_bit_amd as G
         import synthetic as S
         self.spec = spec
         self.d_in, self.d_out = spec.d_in, spec.d_out
-        lin = S.make_linear(spec)
+        lin = S.make_linear(spec, with_codes=host_codes)
         self.q0 = lin.q                                  # host codes of copy 0 (CPU baseline)
         self.s_np, self.z_np, self.x_f32 = lin.s, lin.z, lin.x
         self.L = G.grinqh_layout_init(spec.d_in, spec.d_out, spec.b_max)
         self.planes = []
         for c in range(n_copies):
-            q = lin.q if c == 0 else S.gen_codes(spec, role=10 + c)
-            qd = torch.from_numpy(q).to(dev)
+            if c == 0 and host_codes:
+                qd = torch.from_numpy(lin.q).to(dev)
+            else:
+                g = torch.Generator(device=dev)
+                g.manual_seed(S.torch_seed(spec.key, 10 + c))
+                qd = torch.randint(0, 1 << spec.b_max, (spec.d_out, spec.d_in), generator=g, dtype=torch.uint8,
+                                   device=dev)
             _, pl = G.pack(qd, spec.b_max)
             self.planes.append(pl)
             del qd
@@ -108,32 +137,35 @@ class Shape:
         self.x = torch.from_numpy(lin.x_bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
         self.ws = G.new_workspace(self.L, dev)
         self.y = torch.empty(spec.d_out, dtype=torch.bfloat16, device=dev)
-        # thresholds per effective-bits target (same codes, scales and x for every target)
         self.theta = {}
         self.theta_np = {}
+        self.bits = {}
+        self.req = {}
         for eff, sp in effs.items():
             th = S.make_linear(sp, with_codes=False).theta
             self.theta_np[eff] = th
             self.theta[eff] = torch.from_numpy(th).to(dev)
-        self.bits = {}
-        self.req = {}
-        for eff in effs:
             bits, _, _ = G.assign_bits(self.L, self.x, self.theta[eff])
             torch.cuda.synchronize()
             b = bits.cpu().numpy()
             self.bits[eff] = b
             self.req[eff] = required_bytes(b, self.d_out)
+        self.n_copies = n_copies
 
     def launch(self, copy: int, eff) -> None:
         import input_adaptive_bit_amd as G
-        G.grinqh_gemv(self.L, self.x, self.theta[eff], self.planes[copy], self.s, self.z, self.y, self.ws)
+        G.grinqh_gemv(self.L, self.x, self.theta[eff], self.planes[copy % self.n_copies], self.s, self.z, self.y,
+                      self.ws)
 
     def operands(self, copy: int, eff):
-        return (self.x, self.theta[eff], self.planes[copy], self.s, self.z, self.y)
+        return (self.x, self.theta[eff], self.planes[copy % self.n_copies], self.s, self.z, self.y)
+
+    def eff_bits(self, eff) -> float:
+        return float(self.bits[eff].astype(np.float64).mean())
 
 
-class Step:
-    """The three linears as one grinqh_gemv_group launch."""
+class GroupStep:
+    """The linears of a step as one grinqh_gemv_group launch."""
 
     def __init__(self, shapes, dev):
         import input_adaptive_bit_amd as G
@@ -197,7 +229,8 @@ def capture(fn):
 
 
 def time_graph(g, reps: int = 1) -> float:
-    """Milliseconds for `reps` replays, events on the current stream."""
+    """Milliseconds for `reps` replays, events on the current stream (the
+    stream the library's kernels are launched on)."""
     import torch
     st = torch.cuda.Event(enable_timing=True)
     en = torch.cuda.Event(enable_timing=True)
@@ -208,6 +241,70 @@ def time_graph(g, reps: int = 1) -> float:
     en.record()
     torch.cuda.synchronize()
     return st.elapsed_time(en)
+
+
+def time_per_rep(fn_rep, reps: int) -> float:
+    """Microseconds per repetition of fn_rep(r), r = 0 .. reps-1, captured in
+    one graph: the median of three replays after one warm replay."""
+    g = capture(lambda: [fn_rep(r) for r in range(reps)])
+    time_graph(g)
+    ts = sorted(time_graph(g) for _ in range(3))
+    del g
+    return ts[1] * 1e3 / reps
+
+
+def point(us: float, req: float, **extra) -> dict:
+    gbs = req / (us * 1e-6) / 1e9
+    return dict({"us": round(us, 3), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                 "required_MB": round(req / 1e6, 3)}, **extra)
+
+
+def sweep_shapes(shapes, effs, reps, group=None, dense_key=None):
+    """Per effective-bits target: each linear in its own launch, the linears
+    one after another (the step), and optionally one group launch."""
+    out = {}
+    for e in effs:
+        row = {}
+        for sh in shapes:
+            t = time_per_rep(lambda r, sh=sh, e=e: sh.launch(r, e), reps)
+            row[f"{sh.d_in}x{sh.d_out}"] = point(t, sh.req[e], eff_bits=round(sh.eff_bits(e), 4))
+        req = sum(sh.req[e] for sh in shapes)
+        t = time_per_rep(lambda r, e=e: [sh.launch(r, e) for sh in shapes], reps)
+        row["step (one launch per linear)"] = point(t, req)
+        if group is not None:
+            t = time_per_rep(lambda r, e=e: group.launch(r, e), reps)
+            row["step (one group launch)"] = point(t, req)
+        key = str(e) if e != dense_key else f"{e} (dense)"
+        out[key] = row
+        log(f"  eff {key}: " + ", ".join(f"{k} {v['us']} us {v['GB/s']} GB/s" for k, v in row.items()))
+    return out
+
+
+def fits(sweep, shape_keys):
+    """Latency against effective bits per linear: intercept (fixed cost of a
+    launch), slope, and the marginal bandwidth the slope implies."""
+    out = {}
+    for k in shape_keys:
+        xs = [row[k]["eff_bits"] for row in sweep.values()]
+        us = [row[k]["us"] for row in sweep.values()]
+        mb = [row[k]["required_MB"] for row in sweep.values()]
+        a, b = fit_line(xs, us)
+        a_mb, b_mb = fit_line(mb, us)
+        out[k] = {"intercept_us": round(a, 3), "us_per_bit": round(b, 3),
+                  "marginal_GB/s": round(1e3 / b_mb, 1) if b_mb > 0 else None,
+                  "intercept_share_at_3_bits": round(a / (a + 3 * b), 3)}
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline_rows():
@@ -230,8 +327,6 @@ def cpu_baseline_rows():
     rows["prefill"] = {"value": round(8 / el, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
                       "TFLOP/s": round(2.0 * 8 * 4096 * 16384 / el / 1e12, 6),
                       "sample": f"8 tokens through 4096->16384 at b_max 8 (numpy fp64 oracle, one thread, {el:.1f} s)"}
-    # the offline rows: threshold calibration of 128 x 4096 bf16 samples and
-    # RTN quantisation of a 4096 x 4096 bf16 matrix
     xc = S.bf16_bits_to_f32(S.f32_to_bf16_bits(rng.standard_t(3, 128 * 4096).astype(np.float32)))
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
@@ -248,27 +343,56 @@ def cpu_baseline_rows():
     return rows
 
 
-def cpu_baseline(shapes, eff, seconds: float, prefill: bool = True):
+def _oracle_pass(shapes, eff, threads: int):
+    """One pass of the C oracle over the step's linears; with threads > 1 the
+    output rows of each linear are split into `threads` contiguous blocks,
+    each computed by the unchanged oracle in its own host thread (the C call
+    releases the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import c_oracle
-    per_step = sum(sh.req[eff] for sh in shapes)
-    t0 = time.perf_counter()
-    passes = 0
-    while True:
+    if threads == 1:
+        return [c_oracle.gemv(sh.x_f32, sh.theta_np[eff], sh.q0, sh.s_np, sh.z_np, sh.spec.b_max) for sh in shapes]
+    ys = []
+    with ThreadPoolExecutor(threads) as ex:
         for sh in shapes:
-            c_oracle.gemv(sh.x_f32, sh.theta_np[eff], sh.q0, sh.s_np, sh.z_np, sh.spec.b_max)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+            edges = np.linspace(0, sh.d_out, threads + 1).astype(int)
+            futs = [ex.submit(c_oracle.gemv, sh.x_f32, sh.theta_np[eff], sh.q0[a:b], sh.s_np[a:b], sh.z_np[a:b],
+                              sh.spec.b_max) for a, b in zip(edges[:-1], edges[1:])]
+            ys.append(np.concatenate([f.result() for f in futs]))
+    return ys
+
+
+def cpu_baseline(shapes, eff, seconds: float, rows: bool = True):
+    """The plain fp64 C oracle, as it stands, on whole passes of the step's
+    linears: first on one host thread, then on every host core."""
+    per_step = sum(sh.req[eff] for sh in shapes)
+    cores = os.cpu_count() or 1
+    res = {}
+    for threads in (1, cores):
+        t0 = time.perf_counter()
+        passes = 0
+        while True:
+            _oracle_pass(shapes, eff, threads)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= seconds / 2:
+                break
+        res[threads] = (passes, el)
+    p1, e1 = res[1]
+    pn, en = res[cores]
     out = {
-        "value": round(per_step * passes / el / 1e9, 4),
+        "value": round(per_step * pn / en / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"{passes} full passes of the 3 linears at ~{eff} eff. bits "
-                   f"(plain fp64 C oracle, one thread, {el:.1f} s)"),
+        "sample": (f"{pn} full passes of the 3 linears at ~{eff} eff. bits on {cores} host threads "
+                   f"(plain fp64 C oracle, output rows split into {cores} blocks, {en:.1f} s)"),
+        "cpu_model": cpu_model(),
+        "os_cpu_count": cores,
+        "one_thread": {"value": round(per_step * p1 / e1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                       "sample": f"{p1} full passes on one thread ({e1:.1f} s)"},
     }
-    if prefill:
+    if rows:
         out.update(cpu_baseline_rows())
     return out
 
@@ -279,14 +403,17 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--eff", type=int, default=3, choices=[2, 3, 4, 8])
-    ap.add_argument("--sweep-reps", type=int, default=64, help="launches per (eff, shape) sweep point")
+    ap.add_argument("--sweep-reps", type=int, default=64, help="launches per sweep point")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-b4", action="store_true", help="skip the b_max 4 sweep")
     ap.add_argument("--no-b6", action="store_true", help="skip the b_max 6 sweep")
+    ap.add_argument("--no-70b", action="store_true", help="skip the 70B shapes (4.3 GB of planes)")
     ap.add_argument("--no-decode-step", action="store_true",
                     help="skip the 32-layer decode-step measurement (7.0 GB of planes)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-stage GEMM timing")
+    ap.add_argument("--no-offline", action="store_true", help="skip calibration and RTN timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copies", type=int, default=0, help="weight copies (0: enough for 512 MB)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run a plain elementwise fp32 kernel (torch.neg) that reads and "
@@ -309,27 +436,23 @@ def main() -> int:
         return 1
     G.load()
     dev = torch.device("cuda:0")
-    effs = {e: None for e in (2, 3, 4, 8)}
+    effs = (2, 3, 4, 8)
     per_eff_specs = {e: S.llama8b_linears(e) for e in effs}
-    set_bytes = sum(4096 * 4096 + 4096 * 14336 + 14336 * 4096 for _ in [0])   # b_max 8: 1 byte/weight
+    set_bytes = sum(di * do for di, do in S.LLAMA8B_SHAPES)      # b_max 8: 1 byte per weight
     n_copies = args.copies or max(1, math.ceil(2 * MALL_BYTES / set_bytes))
     log(f"setup: {n_copies} weight copies of {set_bytes / 1e6:.1f} MB")
-    shapes = []
-    for k in range(3):
-        sp = {e: per_eff_specs[e][k] for e in effs}
-        shapes.append(Shape(sp[args.eff], n_copies, dev, sp))
+    shapes = [Shape(per_eff_specs[args.eff][k], n_copies, dev, {e: per_eff_specs[e][k] for e in effs})
+              for k in range(3)]
     eff = args.eff
-    step = Step(shapes, dev)
 
-    def steps_fn(n, e=None):
-        e = eff if e is None else e
-
+    def steps_fn(n):
         def run():
             for st in range(n):
-                step.launch(st % n_copies, e)
+                for sh in shapes:
+                    sh.launch(st, eff)
         return run
 
-    # warmup (eager, fills caches/JIT paths), then the two graphs
+    # warmup (eager), then the timed graph of exactly K steps
     steps_fn(2)()
     torch.cuda.synchronize()
     g_warm = capture(steps_fn(max(1, args.warmup))) if args.warmup > 0 else None
@@ -338,12 +461,13 @@ def main() -> int:
         time_graph(g_warm)
     torch.cuda.synchronize()
     ms = time_graph(g_timed)
+    del g_timed, g_warm
     ms_per_step = ms / args.steps
     step_bytes = sum(sh.req[eff] for sh in shapes)
     value_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    n_launch = args.steps                      # one kernel launch per step
+    n_launch = 3 * args.steps                  # one kernel launch per linear
     avg_launch_us = ms * 1e3 / n_launch
-    bytes_per_launch = step_bytes
+    bytes_per_launch = step_bytes / 3
     achieved = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
     eff_real = float(np.sum([sh.bits[eff].astype(np.int64).sum() * sh.d_out for sh in shapes]) /
                      np.sum([sh.d_in * sh.d_out for sh in shapes]))
@@ -360,61 +484,59 @@ def main() -> int:
             f"(each reads {args.copy_probe_mib} MiB, writes {args.copy_probe_mib} MiB)")
         del src, dst
 
-    sweep = {}
+    reps = args.sweep_reps
+    sweep, sweep_fit = {}, {}
     if not args.no_sweep:
-        for e in effs:
-            row = {}
-            g = capture(steps_fn(args.sweep_reps, e))
-            time_graph(g)
-            t = time_graph(g) * 1e3 / args.sweep_reps
-            req = sum(sh.req[e] for sh in shapes)
-            row["step (3 linears, one launch)"] = {
-                "us": round(t, 3), "GB/s": round(req / t / 1e3, 1),
-                "frac_of_peak": round(req / t / 1e3 / HBM_PEAK_GBS, 4), "required_MB": round(req / 1e6, 3)}
-            for sh in shapes:
-                def one(sh=sh, e=e):
-                    for r in range(args.sweep_reps):
-                        sh.launch(r % n_copies, e)
-                g = capture(one)
-                time_graph(g)
-                t = time_graph(g) * 1e3 / args.sweep_reps
-                gbs = sh.req[e] / (t * 1e-6) / 1e9
-                row[f"{sh.d_in}x{sh.d_out} (own launch)"] = {
-                    "us": round(t, 3), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-                    "eff_bits": round(float(sh.bits[e].mean()), 4), "required_MB": round(sh.req[e] / 1e6, 3)}
-            sweep[str(e) if e != 8 else "8 (dense)"] = row
-            log(f"sweep eff {e}: " + ", ".join(f"{k} {v['us']} us {v['GB/s']} GB/s" for k, v in row.items()))
+        log("sweep b_max 8:")
+        group = GroupStep(shapes, dev)
+        sweep = sweep_shapes(shapes, effs, reps, group=group, dense_key=8)
+        sweep_fit = fits(sweep, [f"{sh.d_in}x{sh.d_out}" for sh in shapes])
+        log(f"  fit: {sweep_fit}")
+        del group
+
+    sweep_b4, fit_b4 = {}, {}
+    if not args.no_sweep and not args.no_b4:
+        effs4 = (1.5, 2, 3, 4)
+        specs4 = {e: S.llama8b_linears_b4(e) for e in effs4}
+        n4 = max(1, math.ceil(2 * MALL_BYTES / (0.5 * set_bytes)))
+        shapes4 = [Shape(specs4[3][k], n4, dev, {e: specs4[e][k] for e in effs4}, host_codes=False)
+                   for k in range(3)]
+        log("sweep b_max 4:")
+        sweep_b4 = sweep_shapes(shapes4, effs4, reps, dense_key=4)
+        fit_b4 = fits(sweep_b4, [f"{sh.d_in}x{sh.d_out}" for sh in shapes4])
+        for e, row in sweep_b4.items():
+            for sh in shapes4:
+                k = f"{sh.d_in}x{sh.d_out}"
+                row[k]["vs_dense_us"] = round(row[k]["us"] / sweep_b4["4 (dense)"][k]["us"], 3)
+        del shapes4
+        torch.cuda.empty_cache()
 
     sweep_b6 = {}
     if not args.no_sweep and not args.no_b6:
-        # the same shapes stored at b_max 6 (levels 0/2/4/6): 0.75 bytes per weight
-        effs6 = {e: None for e in (2, 3, 4, 6)}
+        effs6 = (2, 3, 4, 6)
         specs6 = {e: S.llama8b_linears_b6(e) for e in effs6}
         n6 = max(1, math.ceil(2 * MALL_BYTES / (0.75 * set_bytes)))
-        shapes6 = [Shape(specs6[3][k], n6, dev, {e: specs6[e][k] for e in effs6}) for k in range(3)]
-        step6 = Step(shapes6, dev)
-        for e in effs6:
-            def run6(e=e):
-                for r in range(args.sweep_reps):
-                    step6.launch(r % n6, e)
-            g = capture(run6)
-            time_graph(g)
-            t = time_graph(g) * 1e3 / args.sweep_reps
-            req = sum(sh.req[e] for sh in shapes6)
-            row = {"step (3 linears, one launch)": {
-                "us": round(t, 3), "GB/s": round(req / t / 1e3, 1),
-                "frac_of_peak": round(req / t / 1e3 / HBM_PEAK_GBS, 4), "required_MB": round(req / 1e6, 3),
-                "eff_bits": round(float(np.sum([sh.bits[e].astype(np.int64).sum() * sh.d_out for sh in shapes6]) /
-                                        np.sum([sh.d_in * sh.d_out for sh in shapes6])), 4)}}
-            sweep_b6[str(e) if e != 6 else "6 (dense)"] = row
-            del g
-            log(f"sweep b_max 6 eff {e}: {t:.2f} us, {req / t / 1e3:.1f} GB/s")
-        del step6, shapes6
+        shapes6 = [Shape(specs6[3][k], n6, dev, {e: specs6[e][k] for e in effs6}, host_codes=False)
+                   for k in range(3)]
+        log("sweep b_max 6:")
+        sweep_b6 = sweep_shapes(shapes6, effs6, reps, dense_key=6)
+        del shapes6
+        torch.cuda.empty_cache()
+
+    llama70b = {}
+    if not args.no_sweep and not args.no_70b:
+        effs70 = (2, 3)
+        specs70 = {e: S.llama70b_linears(e) for e in effs70}
+        shapes70 = [Shape(specs70[3][k], 8, dev, {e: specs70[e][k] for e in effs70}, host_codes=False)
+                    for k in range(3)]
+        log(f"70B shapes: 8 copies, {sum(sh.d_in * sh.d_out for sh in shapes70) * 8 / 1e9:.2f} GB of planes")
+        llama70b = sweep_shapes(shapes70, effs70, reps)
+        del shapes70
         torch.cuda.empty_cache()
 
     calibration = {}
-    if not args.no_sweep:
-        # offline threshold calibration: 128 samples of each input width, bf16
+    rtn = {}
+    if not args.no_offline:
         for d_in in (4096, 14336):
             spec = S.LinearSpec(d_in, 4096, 8, "t3", "bf16", S.QUANTILES_B8[3], key=(2, 9, 0, d_in))
             xs, _ = S.gen_x_stream(spec)
@@ -423,21 +545,10 @@ def main() -> int:
             ws_c = torch.empty(G.grinqh_calibrate_workspace_bytes(), dtype=torch.uint8, device=dev)
             th_c = torch.empty(4, dtype=torch.float32, device=dev)
             lv = list(spec.quantiles)
-
-            def cal(reps=16):
-                for _ in range(reps):
-                    G.grinqh_calibrate_thresholds(xc, lv, th_c, ws_c)
-            g = capture(cal)
-            time_graph(g)
-            t = time_graph(g) * 1e3 / 16
+            t = time_per_rep(lambda r: G.grinqh_calibrate_thresholds(xc, lv, th_c, ws_c), 16)
             calibration[f"{spec.n_calib}x{d_in} bf16"] = {
                 "values": int(xc.numel()), "us": round(t, 2), "GB/s": round(xc.numel() * 2 / t / 1e3, 1)}
-            del g
             log(f"calibration {spec.n_calib}x{d_in}: {t:.1f} us")
-
-    rtn = {}
-    if not args.no_sweep:
-        # offline RTN quantisation of bf16 weights (reads 2 bytes and writes 1 per weight)
         for di, do in S.LLAMA8B_SHAPES:
             gen = torch.Generator(device=dev)
             gen.manual_seed(S.torch_seed((2, 8, di, do), 0))
@@ -445,16 +556,10 @@ def main() -> int:
             qt = torch.empty((do, di), dtype=torch.uint8, device=dev)
             st_ = torch.empty(do, dtype=torch.float16, device=dev)
             zt = torch.empty(do, dtype=torch.float16, device=dev)
-
-            def quant(reps=8):
-                for _ in range(reps):
-                    G.grinqh_quantize_rtn(wt, 8, qt, st_, zt)
-            g = capture(quant)
-            time_graph(g)
-            t = time_graph(g) * 1e3 / 8
+            t = time_per_rep(lambda r: G.grinqh_quantize_rtn(wt, 8, qt, st_, zt), 8)
             moved = 3.0 * di * do
             rtn[f"{di}x{do}"] = {"us": round(t, 2), "GB/s": round(moved / t / 1e3, 1)}
-            del g, wt, qt
+            del wt, qt
             log(f"rtn {di}x{do}: {t:.1f} us, {moved / t / 1e3:.1f} GB/s")
 
     prefill = {}
@@ -501,32 +606,31 @@ def main() -> int:
             log(f"prefill {M}x{di}->{do} b_max {bm}: {t:.1f} us, {flops / t / 1e6:.1f} TFLOP/s; "
                 f"torch bf16 dense {tt:.1f} us")
 
-    decode_step = {}
+    decode_step, decode_fit = {}, {}
     if not args.no_decode_step:
-        del step
         for sh in shapes:
-            sh.planes = []
+            sh.planes = sh.planes[:1]
+            sh.n_copies = 1
         torch.cuda.empty_cache()
-        ds = DecodeStep(dev, list(effs))
-        for e in effs:
-            def run_ds(e=e, reps=8):
-                for _ in range(reps):
-                    ds.launch(e)
-            g = capture(run_ds)
-            time_graph(g)
-            t = time_graph(g) * 1e3 / 8
+        effs_ds = (2, 3, 4, 6, 8)
+        ds = DecodeStep(dev, list(effs_ds))
+        for e in effs_ds:
+            t = time_per_rep(lambda r, e=e: ds.launch(e), 4)
             gbs = ds.req[e] / (t * 1e-6) / 1e9
             decode_step[str(e) if e != 8 else "8 (dense)"] = {
                 "us": round(t, 2), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-                "required_GB": round(ds.req[e] / 1e9, 4), "launches": len(ds.ops)}
-            del g
+                "required_GB": round(ds.req[e] / 1e9, 4), "launches": len(ds.ops),
+                "us_per_launch": round(t / len(ds.ops), 3)}
             log(f"decode step eff {e}: {t:.1f} us, {gbs:.1f} GB/s")
+        a, b = fit_line([v["required_GB"] for v in decode_step.values()], [v["us"] for v in decode_step.values()])
+        decode_fit = {"intercept_us": round(a, 1), "intercept_us_per_launch": round(a / len(ds.ops), 3),
+                      "marginal_GB/s": round(1e3 / b, 1) if b > 0 else None}
         del ds
         torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(shapes, eff, args.cpu_seconds, prefill=not args.no_prefill)
+        cpu = cpu_baseline(shapes, eff, args.cpu_seconds, rows=not args.no_prefill)
         log(f"cpu baseline: {cpu}")
 
     out = {
@@ -543,8 +647,9 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": ("8B-shaped decode linears 4096->4096, 4096->14336, 14336->4096; b_max 8; "
-                         f"~{eff} eff. bits; batch 1; bf16 x ~ t(3), bf16 y; fp16 per-output s, z"),
+            "workload": ("8B-shaped decode linears 4096->4096, 4096->14336, 14336->4096, one grinqh_gemv "
+                         f"launch each; b_max 8; ~{eff} eff. bits; batch 1; bf16 x ~ t(3), bf16 y; "
+                         "fp16 per-output s, z"),
             "global_batch": 1,
             "seq_len": 1,
             "eff_bits_realized": round(eff_real, 4),
@@ -559,16 +664,21 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": counted_traffic(eff),
-            "kernel": "gemv_kernel (one grinqh_gemv_group launch per step)",
+            "kernel": "gemv_kernel (three grinqh_gemv launches per step; per-launch average)",
             "avg_launch_us": round(avg_launch_us, 3),
             "bytes_per_launch": int(bytes_per_launch),
         },
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "sweep_fit_us_vs_eff_bits": sweep_fit,
+        "sweep_b_max_4": sweep_b4,
+        "sweep_b_max_4_fit": fit_b4,
         "sweep_b_max_6": sweep_b6,
+        "llama70b_shapes": llama70b,
         "threshold_calibration": calibration,
         "rtn_quantisation_b_max_8": rtn,
         "decode_step_32_layers": decode_step,
+        "decode_step_fit_us_vs_GB": decode_fit,
         "prefill_gemm": prefill,
     }
     print(json.dumps(out), flush=True)

@@ -225,12 +225,19 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     __shared__ float red[NW][T];             // one partial row per worker
 
     // ---- locate the GEMV and the (tile, slice) of this workgroup
+    // Workgroup b is dispatched to XCD b % 8.  The items (GEMV, tile, slice)
+    // are numbered tile-major and each XCD takes a contiguous run of them, so
+    // the slices of a tile meet in one XCD's L2 (a tile may straddle two).
+    const int W = static_cast<int>(gridDim.x);
+    const int xq = W >> 3, xr = W & 7;
+    const int bx = static_cast<int>(blockIdx.x) & 7, br = static_cast<int>(blockIdx.x) >> 3;
+    const int item = bx * xq + min(bx, xr) + br;
     int d = 0;
-    while (d + 1 < args.n && static_cast<int>(blockIdx.x) >= args.g[d + 1].wg_begin) ++d;
+    while (d + 1 < args.n && item >= args.g[d + 1].wg_begin) ++d;
     const GemvDesc& D = args.g[d];
-    const int local = static_cast<int>(blockIdx.x) - D.wg_begin;
-    const int tile = local % D.n_tiles;
-    const int split = local / D.n_tiles;
+    const int local = item - D.wg_begin;
+    const int tile = local / D.n_splits;
+    const int split = local % D.n_splits;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -359,9 +366,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
         z_j[k] = f16_to_f32(D.z[jc]);
     }
     // The tile's partial A_j + C_slice and S_slice go to the workspace with
-    // returning agent-scope atomic adds; consuming their results makes the
-    // wave wait until each add has been performed at the device's coherence
-    // point for that address, before the arrival count below is taken.
+    // agent-scope fp32 atomic adds.
     unsigned* ctrl = D.ctrl + static_cast<size_t>(tile) * kCtrlWords;   // own 256-byte line per tile
     float* ssum = reinterpret_cast<float*>(ctrl + 1);
 #pragma unroll
@@ -375,25 +380,30 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
         for (int h = NW / 2; h > 0; h /= 2)
 #pragma unroll
             for (int w = 0; w < h; ++w) v[w] += v[w + h];
-        const float old = __hip_atomic_fetch_add(ws_acc + o, v[0] + c_slice, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("" ::"v"(old));
+        unsafeAtomicAdd(ws_acc + o, v[0] + c_slice);
     }
-    if (tid == 0) {
-        const float old = __hip_atomic_fetch_add(ssum, s_slice, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("" ::"v"(old));
-    }
+    if (tid == 0) unsafeAtomicAdd(ssum, s_slice);
 
-    // ---- last workgroup of the tile applies the epilogue.  Every thread's
-    // adds are complete (their results were consumed above) before the
-    // barrier, and the arrival count is taken after it, so the workgroup that
-    // sees n_splits - 1 earlier arrivals finds every slice's adds performed.
-    // It takes S and the row back with atomic exchanges against zero (read
-    // and clear in one step at the same coherence point as the adds), after
-    // an agent-scope acquire fence.  S is taken once, by thread 0, and handed
-    // to the other threads through LDS behind a barrier.  (No device-scope
-    // fence on the add side: a __threadfence writes back and invalidates the
-    // L2 for every workgroup, which serialises the whole grid.)
+    // ---- last workgroup of the tile applies the epilogue.
+    //
+    // Ordering.  Every access to the workspace row, the S slot and the
+    // arrival counter is an agent-scope atomic read-modify-write, and such
+    // atomics are performed at one point per address for the whole device
+    // (every XCD's adds to an address combine there).  A wave's vector
+    // memory counter counts its atomic adds until the memory system
+    // acknowledges them as performed, so after s_waitcnt 0 each thread's
+    // adds are done; the barrier then waits for every thread, and only
+    // after it does thread 0 take the arrival count.  The workgroup that
+    // sees n_splits - 1 earlier arrivals therefore finds every slice's adds
+    // performed, and reads them with atomic exchanges against zero (read
+    // and clear in one step) issued after it saw the count.  S is taken
+    // once, by thread 0, and handed to the other threads through LDS behind
+    // a barrier.  No release or acquire fence is used: at agent scope they
+    // write back or invalidate the whole L2 of the XCD, which measured about
+    // twice the time of a whole launch of this kernel.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
     if (tid == 0) {
         const unsigned prev = __hip_atomic_fetch_add(ctrl, 1u, __ATOMIC_RELAXED,
@@ -401,7 +411,6 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
         const int last = (prev == static_cast<unsigned>(D.n_splits - 1)) ? 1 : 0;
         L.is_last = last;
         if (last) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             L.S = __hip_atomic_exchange(ssum, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // every arrival of this call has been counted: reset for the next call
             __hip_atomic_store(ctrl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -409,7 +418,6 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     }
     __syncthreads();
     if (!L.is_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const float S = L.S;
     const int j0 = tile * T;
 #pragma unroll

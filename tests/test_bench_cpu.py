@@ -24,3 +24,30 @@ def test_cpu_baseline_rows_report_the_oracle():
     for v in rows.values():
         assert v["kind"] == "oracle" and v["cores"] == 1 and v["value"] > 0
     json.dumps(rows)
+
+
+def test_oracle_pass_on_all_cores_matches_one_thread():
+    """The all-cores CPU baseline splits each linear's output rows over host
+    threads running the unchanged C oracle; the outputs equal one thread's."""
+    import types
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    import synthetic as S
+    shapes = []
+    for di, do in ((300, 1000), (64, 65)):
+        spec = S.LinearSpec(di, do, 8, "t3", "bf16", S.QUANTILES_B8[3], key=(9, di, do, 0))
+        lin = S.make_linear(spec)
+        shapes.append(types.SimpleNamespace(x_f32=lin.x, theta_np={3: lin.theta}, q0=lin.q, s_np=lin.s, z_np=lin.z,
+                                            spec=spec, d_out=do))
+    one = bench._oracle_pass(shapes, 3, 1)
+    many = bench._oracle_pass(shapes, 3, 5)
+    for a, b in zip(one, many):
+        assert np.array_equal(a, b)
+
+
+def test_fit_line_recovers_a_line():
+    sys.path.insert(0, ROOT)
+    import bench
+    a, b = bench.fit_line([2, 3, 4, 8], [10.0 + 2 * 1.5, 10.0 + 3 * 1.5, 10.0 + 4 * 1.5, 10.0 + 8 * 1.5])
+    assert abs(a - 10.0) < 1e-9 and abs(b - 1.5) < 1e-9
