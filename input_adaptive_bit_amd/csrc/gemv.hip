@@ -191,7 +191,7 @@ __device__ __forceinline__ void compute_batch(float (&acc)[16 * V], const Batch<
 // is issued before any decoding starts, and a batch holds a typical slice's
 // share of its bucket, so a workgroup waits for about one memory round trip.
 template <int Pb>
-struct BatchSize { static constexpr int U = Pb == 4 ? 1 : Pb == 3 ? 3 : Pb == 2 ? 5 : 6; };
+struct BatchSize { static constexpr int U = Pb == 4 ? 2 : Pb == 3 ? 3 : Pb == 2 ? 5 : 6; };
 
 template <int P, int Pb, int V, int G>
 struct Bucket {
@@ -202,7 +202,8 @@ struct Bucket {
     // begin, end: the bucket's entries (wave-uniform)
     __device__ __forceinline__ void first(const SliceLists& L, int begin, int end_, int worker,
                                           const PlaneSrc& src) {
-        e = begin + worker;
+        // the wave that takes a bucket's uneven last round rotates with the bucket
+        e = begin + (worker + (Pb - 1) * G) % stride;
         end = end_;
         load_batch<P, Pb, V, U>(B, L, e, stride, end, src);
     }
@@ -222,7 +223,11 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     constexpr int T = LG * 16 * V;           // outputs per tile
     constexpr int NW = kWaves * G;           // workers (lane groups) per workgroup
     __shared__ SliceLists L;
-    __shared__ float red[NW][T];             // one partial row per worker
+    // One partial row per worker; a lane's 16 * V outputs are stored with a
+    // stride of 16 * V + 4 floats, so that the lanes of a wave's 16-byte
+    // stores fall in different LDS banks.
+    constexpr int RSTR = 16 * V + 4;
+    __shared__ float red[NW][LG * RSTR];
 
     // ---- locate the GEMV and the (tile, slice) of this workgroup
     // Workgroup b is dispatched to XCD b % 8.  The items (GEMV, tile, slice)
@@ -344,7 +349,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     // thread sums the NW copies of its outputs in worker order (fixed order)
 #pragma unroll
     for (int o = 0; o < 16 * V; o += 4)
-        *reinterpret_cast<float4*>(&red[worker][r * 16 * V + o]) =
+        *reinterpret_cast<float4*>(&red[worker][r * RSTR + o]) =
             make_float4(acc[o], acc[o + 1], acc[o + 2], acc[o + 3]);
     __syncthreads();
     float s_slice = L.red_s[0], c_slice = L.red_c[0];
@@ -375,7 +380,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
         // all NW partials first, then a fixed-order pairwise sum
         float v[NW];
 #pragma unroll
-        for (int w = 0; w < NW; ++w) v[w] = red[w][o];
+        for (int w = 0; w < NW; ++w) v[w] = red[w][(o / (16 * V)) * RSTR + o % (16 * V)];
 #pragma unroll
         for (int h = NW / 2; h > 0; h /= 2)
 #pragma unroll
@@ -396,9 +401,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     // after it does thread 0 take the arrival count.  The workgroup that
     // sees n_splits - 1 earlier arrivals therefore finds every slice's adds
     // performed, and reads them with atomic exchanges against zero (read
-    // and clear in one step) issued after it saw the count.  S is taken
-    // once, by thread 0, and handed to the other threads through LDS behind
-    // a barrier.  No release or acquire fence is used: at agent scope they
+    // and clear in one step) issued after it saw the count.  No release or acquire fence is used: at agent scope they
     // write back or invalidate the whole L2 of the XCD, which measured about
     // twice the time of a whole launch of this kernel.
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -408,25 +411,29 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     if (tid == 0) {
         const unsigned prev = __hip_atomic_fetch_add(ctrl, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        const int last = (prev == static_cast<unsigned>(D.n_splits - 1)) ? 1 : 0;
-        L.is_last = last;
-        if (last) {
-            L.S = __hip_atomic_exchange(ssum, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            // every arrival of this call has been counted: reset for the next call
-            __hip_atomic_store(ctrl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        L.is_last = (prev == static_cast<unsigned>(D.n_splits - 1)) ? 1 : 0;
     }
     __syncthreads();
     if (!L.is_last) return;
+    // The row and S are read back (and cleared) at the same time; thread 0
+    // hands S to the other threads through LDS and resets the counter: every
+    // arrival of this call has been counted.
+    float a[OPT];
+#pragma unroll
+    for (int k = 0; k < OPT; ++k)
+        a[k] = __hip_atomic_exchange(ws_acc + tid + k * kThreads, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+        L.S = __hip_atomic_exchange(ssum, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ctrl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
     const float S = L.S;
     const int j0 = tile * T;
 #pragma unroll
     for (int k = 0; k < OPT; ++k) {
-        const int o = tid + k * kThreads;
-        const int j = j0 + o;
-        const float a = __hip_atomic_exchange(ws_acc + o, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int j = j0 + tid + k * kThreads;
         if (j < D.d_out) {
-            const float yv = s_j[k] * a + z_j[k] * S;
+            const float yv = s_j[k] * a[k] + z_j[k] * S;
             if (D.y_dtype == GRINQH_F32)
                 static_cast<float*>(D.y)[j] = yv;
             else
