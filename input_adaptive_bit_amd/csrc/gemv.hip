@@ -216,8 +216,20 @@ struct Bucket {
     }
 };
 
+// Item number of this workgroup.  Workgroup b is dispatched to XCD b % 8.
+// The items (GEMV, tile, slice) are numbered tile-major and each XCD takes a
+// contiguous run of them, so the slices of a tile meet in one XCD's L2 (a
+// tile may straddle two).
+__device__ __forceinline__ int xcd_item() {
+    const int W = static_cast<int>(gridDim.x);
+    const int xq = W >> 3, xr = W & 7;
+    const int bx = static_cast<int>(blockIdx.x) & 7, br = static_cast<int>(blockIdx.x) >> 3;
+    return bx * xq + min(bx, xr) + br;
+}
+
+// The work of one workgroup: item `item` of the GEMV described by D.
 template <int P, int V, int G>
-__global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs args) {
+__device__ __forceinline__ void gemv_item(const GemvDesc& D, int item) {
     constexpr int b_max = 2 * P;
     constexpr int LG = kWave / G;            // lanes per group
     constexpr int T = LG * 16 * V;           // outputs per tile
@@ -229,17 +241,13 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     constexpr int RSTR = 16 * V + 4;
     __shared__ float red[NW][LG * RSTR];
 
-    // ---- locate the GEMV and the (tile, slice) of this workgroup
-    // Workgroup b is dispatched to XCD b % 8.  The items (GEMV, tile, slice)
-    // are numbered tile-major and each XCD takes a contiguous run of them, so
-    // the slices of a tile meet in one XCD's L2 (a tile may straddle two).
-    const int W = static_cast<int>(gridDim.x);
-    const int xq = W >> 3, xr = W & 7;
-    const int bx = static_cast<int>(blockIdx.x) & 7, br = static_cast<int>(blockIdx.x) >> 3;
-    const int item = bx * xq + min(bx, xr) + br;
-    int d = 0;
-    while (d + 1 < args.n && item >= args.g[d + 1].wg_begin) ++d;
-    const GemvDesc& D = args.g[d];
+    // Every field of the descriptor is loaded now, while x and theta are on
+    // their way, rather than where the reduction and epilogue first use it
+    // (a kernel-argument load there waits a whole memory round trip).
+    asm volatile("" ::"s"(D.x), "s"(D.theta), "s"(D.planes), "s"(D.s), "s"(D.z), "s"(D.y), "s"(D.acc),
+                 "s"(D.ctrl));
+    asm volatile("" ::"s"(D.d_in), "s"(D.d_out), "s"(D.row_words), "s"(D.chunk), "s"(D.n_splits),
+                 "s"(D.n_tiles), "s"(D.x_dtype), "s"(D.y_dtype));
     const int local = item - D.wg_begin;
     const int tile = local / D.n_splits;
     const int split = local % D.n_splits;
@@ -442,10 +450,43 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs 
     }
 }
 
+// A group of GEMVs: the workgroup finds its member from the item number.
+template <int P, int V, int G>
+__global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_kernel(GemvGroupArgs args) {
+    const int item = xcd_item();
+    int d = 0;
+    while (d + 1 < args.n && item >= args.g[d + 1].wg_begin) ++d;
+    const GemvDesc D = args.g[d];
+    gemv_item<P, V, G>(D, item);
+}
+
+// One GEMV (grinqh_gemv): the descriptor is the whole kernel argument.
+template <int P, int V, int G>
+__global__ __launch_bounds__(kThreads, kWgPerCu) void gemv_one_kernel(GemvDesc D) {
+    gemv_item<P, V, G>(D, xcd_item());
+}
+
 template <int P, int V, int G>
 hipError_t launch_t(const GemvGroupArgs& a, int total_wg, hipStream_t stream) {
     gemv_kernel<P, V, G><<<dim3(static_cast<unsigned>(total_wg)), dim3(kThreads), 0, stream>>>(a);
     return hipGetLastError();
+}
+
+template <int P, int V, int G>
+hipError_t launch_one_t(const GemvDesc& d, int total_wg, hipStream_t stream) {
+    gemv_one_kernel<P, V, G><<<dim3(static_cast<unsigned>(total_wg)), dim3(kThreads), 0, stream>>>(d);
+    return hipGetLastError();
+}
+
+template <int P>
+hipError_t launch_one_p(const GemvDesc& d, int G, int total_wg, hipStream_t stream) {
+    switch (G) {
+        case 1: return launch_one_t<P, kV, 1>(d, total_wg, stream);
+        case 2: return launch_one_t<P, kV, 2>(d, total_wg, stream);
+        case 4: return launch_one_t<P, kV, 4>(d, total_wg, stream);
+        case 8: return launch_one_t<P, kV, 8>(d, total_wg, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int P>
@@ -612,10 +653,16 @@ hipError_t launch_gemv(const grinqh_layout& L, const GemvPlan& plan, const void*
                        int x_dtype, const float* theta, const uint32_t* planes,
                        const uint16_t* s, const uint16_t* z, void* y, int y_dtype,
                        void* workspace, hipStream_t stream) {
-    GemvGroupArgs a{};
-    a.n = 1;
-    fill_desc(&a.g[0], L, plan, x, x_dtype, theta, planes, s, z, y, y_dtype, workspace, 0);
-    return launch_gemv_group(L.n_planes, plan.lane_groups, a, plan.n_tiles * plan.n_splits, stream);
+    GemvDesc d{};
+    fill_desc(&d, L, plan, x, x_dtype, theta, planes, s, z, y, y_dtype, workspace, 0);
+    const int wg = plan.n_tiles * plan.n_splits;
+    switch (L.n_planes) {
+        case 1: return launch_one_p<1>(d, plan.lane_groups, wg, stream);
+        case 2: return launch_one_p<2>(d, plan.lane_groups, wg, stream);
+        case 3: return launch_one_p<3>(d, plan.lane_groups, wg, stream);
+        case 4: return launch_one_p<4>(d, plan.lane_groups, wg, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace grinqh
