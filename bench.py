@@ -57,7 +57,7 @@ MALL_BYTES = 256 << 20
 
 KERNEL_SOURCES = ("input_adaptive_bit_amd/csrc/gemv.hip", "input_adaptive_bit_amd/csrc/decode.hpp",
                   "input_adaptive_bit_amd/csrc/device_common.hpp", "input_adaptive_bit_amd/csrc/internal.h")
-COUNTER_SUMMARY = "profiles/gemv_kernel__8b_decode_linears_e3__hbm_counters.md"
+COUNTER_SUMMARY = "profiles/gemv_one_kernel__8b_decode_linears_e3__hbm_counters.md"
 
 
 def log(*a):
@@ -664,7 +664,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": counted_traffic(eff),
-            "kernel": "gemv_kernel (three grinqh_gemv launches per step; per-launch average)",
+            "kernel": "gemv_one_kernel (three grinqh_gemv launches per step; per-launch average)",
             "avg_launch_us": round(avg_launch_us, 3),
             "bytes_per_launch": int(bytes_per_launch),
         },
