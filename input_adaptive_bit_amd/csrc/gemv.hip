@@ -81,13 +81,23 @@ __device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t rsrc, uint32_t
     }
 }
 
+// Factor of decode_unit<Pb> that the slice list's multiplier already holds:
+// all of it for one and two planes (one unit for every output), none for
+// three and four (the unit depends on the byte lane).
+template <int Pb>
+__device__ __forceinline__ constexpr float folded_unit() {
+    return Pb <= 2 ? decode_unit<Pb>(0) : 1.f;
+}
+
 // acc[16 v + t] += x_scaled * code(t) for the 16 outputs t of each of the V
-// word positions, code(t) = value(t) * decode_unit(t & 3) (decode.hpp).
+// word positions, code(t) = value(t) * decode_unit(t & 3) (decode.hpp); xs
+// is x_scaled * folded_unit<Pb>() (every factor a power of two, so the
+// products are those of x_scaled * code).
 template <int Pb, int V>
 __device__ __forceinline__ void accumulate(float (&acc)[16 * V], const uint32_t (&w)[Pb][V], float xs) {
     float a[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) a[k] = xs * decode_unit<Pb>(k);
+    for (int k = 0; k < 4; ++k) a[k] = Pb <= 2 ? xs : xs * decode_unit<Pb>(k);
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         uint32_t pw[Pb];
@@ -102,9 +112,14 @@ __device__ __forceinline__ void accumulate(float (&acc)[16 * V], const uint32_t 
 
 static_assert(kWaves == 4, "one count byte per wave in a word");
 
+// Entries read past a bucket's end: fewer than one batch (U * stride <= 192)
+// beyond the last list entry.  The slice lists are padded so that those
+// reads stay inside them; their values are discarded.
+constexpr int kListPad = 192;
+
 struct SliceLists {
-    uint32_t off[kMaxChunk];   // byte offset of the channel's plane 0 row: i * P * row_bytes
-    float xv[kMaxChunk];       // x_i * 4^(P - Pi): the multiplier of its Pi-plane code
+    uint32_t off[kMaxChunk + kListPad];   // byte offset of the channel's plane 0 row: i * P * row_bytes
+    float xv[kMaxChunk + kListPad];       // x_i * 4^(P - Pi) * folded_unit<Pi>(): multiplier of its Pi-plane code
     uint32_t cnt[4];           // word l, byte w: loaded channels of wave w with l + 1 planes
     float red_s[kWaves], red_c[kWaves];
     int is_last;               // this workgroup arrived last at its tile
@@ -139,12 +154,13 @@ struct Batch {
     uint32_t w[U][Pb][V];
 };
 
-// Issues the plane loads of bucket entries e0, e0 + stride, ... (U of
-// them).  Entries past the bucket end, and lanes whose words lie past the
-// padded row (a tile wider than the layout), load from past the end of the
-// buffer: zeros, no request.  Every other load lies inside its own plane row,
-// so the wave-uniform plane offset never carries an access past the buffer,
-// whether or not the hardware range check counts it.
+// Issues the plane loads of one batch.  Lane group g of a wave takes the
+// bucket entries ew + g + u * stride (u < U), where ew is wave-uniform.
+// Entries past the bucket end, and lanes whose words lie past the padded
+// row (a tile wider than the layout), load from past the end of the buffer:
+// zeros, no request.  Every other load lies inside its own plane row, so the
+// wave-uniform plane offset never carries an access past the buffer, whether
+// or not the hardware range check counts it.
 struct PlaneSrc {
     __amdgpu_buffer_rsrc_t rsrc;
     uint32_t row_bytes;     // bytes per plane row
@@ -157,32 +173,35 @@ struct PlaneSrc {
 // 2^32.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-template <int P, int Pb, int V, int U>
-__device__ __forceinline__ void load_batch(Batch<Pb, V, U>& B, const SliceLists& L, int e0, int stride,
-                                           int end, const PlaneSrc& src) {
+// The lists are read at a per-lane base and compile-time offsets u * stride,
+// so an entry costs no address arithmetic; validity is one compare of the
+// lane group against the wave-uniform number of entries left.
+template <int P, int Pb, int V, int U, int stride>
+__device__ __forceinline__ void load_batch(Batch<Pb, V, U>& B, const uint32_t* offp, int group, int left,
+                                           const PlaneSrc& src) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int e = e0 + u * stride;
-        const bool ok = e < end;
-        const uint32_t base = ok ? L.off[e] + src.lane_bytes : kOutOfRange;
+        const bool ok = group < left - u * stride;
+        const uint32_t base = ok ? offp[u * stride] + src.lane_bytes : kOutOfRange;
 #pragma unroll
         for (int p = 0; p < Pb; ++p)
             load_words<V>(src.rsrc, base, static_cast<uint32_t>(p) * src.row_bytes, B.w[u][p]);
     }
 }
 
-// Decodes the batch slot by slot; a slot that no lane group of the wave has a
-// channel for is skipped as a whole (wave-uniform branch), so small buckets
-// cost only the slots they fill.
-template <int P, int Pb, int V, int U>
-__device__ __forceinline__ void compute_batch(float (&acc)[16 * V], const Batch<Pb, V, U>& B,
-                                              const SliceLists& L, int e0, int stride, int end) {
+// Decodes the batch slot by slot.  With kSkip, a slot that no lane group of
+// the wave has a channel for is skipped as a whole (a scalar test), so small
+// buckets cost only the slots they fill.  A slot's words are then used only
+// behind its test, and the compiler may sink the slot's loads past the decode
+// of the slots before it: the batch is no longer in flight at once.
+template <int P, int Pb, int V, int U, int stride, bool kSkip>
+__device__ __forceinline__ void compute_batch(float (&acc)[16 * V], const Batch<Pb, V, U>& B, const float* xp,
+                                              int group, int left) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int e = e0 + u * stride;
-        const bool ok = e < end;
-        if (__ballot(ok) == 0ull) continue;
-        const float xe = L.xv[ok ? e : 0];      // in range either way: no branch
+        if (kSkip && left - u * stride <= 0) break;
+        const bool ok = group < left - u * stride;
+        const float xe = xp[u * stride];
         accumulate<Pb, V>(acc, B.w[u], ok ? xe : 0.f);
     }
 }
@@ -197,21 +216,29 @@ template <int P, int Pb, int V, int G>
 struct Bucket {
     static constexpr int U = BatchSize<Pb>::U;
     static constexpr int stride = kWaves * G;
+    static_assert(U * stride <= kListPad, "list padding covers a batch past the end");
     Batch<Pb, V, U> B;
-    int e, end;
-    // begin, end: the bucket's entries (wave-uniform)
-    __device__ __forceinline__ void first(const SliceLists& L, int begin, int end_, int worker,
+    int ew, end;            // wave-uniform: lane group 0's entry in the batch, the bucket end
+    // begin, end: the bucket's entries (wave-uniform).  Lane group g of wave
+    // wv is worker wv * G + g; the wave that takes a bucket's uneven last
+    // round rotates with the bucket: wave wv starts at entry
+    // ((wv + Pb - 1) mod 4) * G.
+    __device__ __forceinline__ void first(const SliceLists& L, int begin, int end_, int wv, int group,
                                           const PlaneSrc& src) {
-        // the wave that takes a bucket's uneven last round rotates with the bucket
-        e = begin + (worker + (Pb - 1) * G) % stride;
+        ew = begin + ((wv + Pb - 1) & (kWaves - 1)) * G;
         end = end_;
-        load_batch<P, Pb, V, U>(B, L, e, stride, end, src);
+        load_batch<P, Pb, V, U, stride>(B, &L.off[ew + group], group, end - ew, src);
     }
-    __device__ __forceinline__ void finish(float (&acc)[16 * V], const SliceLists& L, const PlaneSrc& src) {
-        compute_batch<P, Pb, V, U>(acc, B, L, e, stride, end);
-        for (e += stride * U; e < end; e += stride * U) {
-            load_batch<P, Pb, V, U>(B, L, e, stride, end, src);
-            compute_batch<P, Pb, V, U>(acc, B, L, e, stride, end);
+    __device__ __forceinline__ void finish(float (&acc)[16 * V], const SliceLists& L, int group,
+                                           const PlaneSrc& src) {
+        compute_batch<P, Pb, V, U, stride, true>(acc, B, &L.xv[ew + group], group, end - ew);
+        // Later batches exist only for buckets longer than one batch.  The
+        // four-plane ones (every channel in dense mode) decode every slot of
+        // them, so that both channels of a batch stay in flight together; the
+        // empty slots of a bucket's last batch cost little next to the rest.
+        for (ew += stride * U; ew < end; ew += stride * U) {
+            load_batch<P, Pb, V, U, stride>(B, &L.off[ew + group], group, end - ew, src);
+            compute_batch<P, Pb, V, U, stride, (Pb < 4)>(acc, B, &L.xv[ew + group], group, end - ew);
         }
     }
 };
@@ -248,26 +275,36 @@ __device__ __forceinline__ void gemv_item(const GemvDesc& D, int item) {
                  "s"(D.ctrl));
     asm volatile("" ::"s"(D.d_in), "s"(D.d_out), "s"(D.row_words), "s"(D.chunk), "s"(D.n_splits),
                  "s"(D.n_tiles), "s"(D.x_dtype), "s"(D.y_dtype));
-    const int local = item - D.wg_begin;
-    const int tile = local / D.n_splits;
-    const int split = local % D.n_splits;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
-
     float th[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < P; ++k) th[k] = D.theta[k];
+    const int local = item - D.wg_begin;
+    const int tile = D.split_magic ? static_cast<int>(__umulhi(static_cast<uint32_t>(local), D.split_magic))
+                                   : local / D.n_splits;
+    const int split = local - tile * D.n_splits;
 
     // ---- prologue: bit assignment and bucket sort of the slice (key design 1)
+    // x is read through a buffer resource, threads past the slice from past
+    // its end (zero, no request), so no branch holds the loads back.
     const int i0 = split * D.chunk;
     const int cnt = min(D.chunk, D.d_in - i0);
-    float xv = 0.f;
-    int pi = 0;
-    if (tid < cnt) {
-        xv = load_x(D.x, D.x_dtype, i0 + tid);
-        pi = bits_of<P>(xv, th) >> 1;
+    const bool mine = tid < cnt;
+    float xv;
+    {
+        const int esz = D.x_dtype == 0 ? 2 : 4;
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<void*>(D.x), static_cast<short>(0), D.d_in * esz, 0x00020000);
+        const uint32_t xo = mine ? static_cast<uint32_t>(i0 + tid) * esz : kOutOfRange;
+        if (D.x_dtype == 0)
+            xv = bf16_to_f32(static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(xr, xo, 0, 0)));
+        else
+            xv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xr, xo, 0, 0));
     }
+    // (with theta_0 <= 0 a zero x would get bits: threads past the slice get none)
+    const int pi = mine ? bits_of<P>(xv, th) >> 1 : 0;
     int rank = 0;
 #pragma unroll
     for (int l = 0; l < P; ++l) {
@@ -299,7 +336,8 @@ __device__ __forceinline__ void gemv_item(const GemvDesc& D, int item) {
         for (int l = 1; l < P; ++l) pos = pi == l + 1 ? below[l] : pos;
         pos += rank;
         L.off[pos] = static_cast<uint32_t>(i0 + tid) * (P * static_cast<uint32_t>(D.row_words) * 4u);
-        L.xv[pos] = xv * static_cast<float>(1u << (2 * (P - pi)));
+        const float unit = pi == 1 ? folded_unit<1>() : pi == 2 ? folded_unit<2>() : 1.f;
+        L.xv[pos] = xv * (static_cast<float>(1u << (2 * (P - pi))) * unit);
     }
     __syncthreads();
 
@@ -326,11 +364,11 @@ __device__ __forceinline__ void gemv_item(const GemvDesc& D, int item) {
     // then keeps a part of its loads in the CU's queue instead of all of
     // them, so the resident workgroups are served side by side rather than
     // one after another.
-    if constexpr (P >= 4) k4.first(L, start[3], start[4], worker, src);
-    if constexpr (P >= 3) k3.first(L, start[2], start[3], worker, src);
+    if constexpr (P >= 4) k4.first(L, start[3], start[4], wv, group, src);
+    if constexpr (P >= 3) k3.first(L, start[2], start[3], wv, group, src);
     if constexpr (P <= 2) {
-        if constexpr (P >= 2) k2.first(L, start[1], start[2], worker, src);
-        k1.first(L, start[0], start[1], worker, src);
+        if constexpr (P >= 2) k2.first(L, start[1], start[2], wv, group, src);
+        k1.first(L, start[0], start[1], wv, group, src);
     }
 
     // slice sums S and C over loaded channels (fixed-order reduction), while
@@ -343,14 +381,14 @@ __device__ __forceinline__ void gemv_item(const GemvDesc& D, int item) {
             L.red_c[wv] = c_w;
         }
     }
-    if constexpr (P >= 4) k4.finish(acc, L, src);
+    if constexpr (P >= 4) k4.finish(acc, L, group, src);
     if constexpr (P >= 3) {
-        k2.first(L, start[1], start[2], worker, src);
-        k3.finish(acc, L, src);
-        k1.first(L, start[0], start[1], worker, src);
+        k2.first(L, start[1], start[2], wv, group, src);
+        k3.finish(acc, L, group, src);
+        k1.first(L, start[0], start[1], wv, group, src);
     }
-    if constexpr (P >= 2) k2.finish(acc, L, src);
-    k1.finish(acc, L, src);
+    if constexpr (P >= 2) k2.finish(acc, L, group, src);
+    k1.finish(acc, L, group, src);
 
 
     // ---- reduction: every worker stores its partial row to LDS, then each
@@ -636,6 +674,12 @@ void fill_desc(GemvDesc* g, const grinqh_layout& L, const GemvPlan& plan, const 
     g->wg_begin = wg_begin;
     g->x_dtype = x_dtype;
     g->y_dtype = y_dtype;
+    // The multiply-high quotient is exact while item * n_splits < 2^32; for
+    // one split, or a launch too large for that, the kernel divides instead.
+    const uint64_t items = static_cast<uint64_t>(plan.n_tiles) * static_cast<uint64_t>(plan.n_splits);
+    g->split_magic = plan.n_splits > 1 && items * static_cast<uint64_t>(plan.n_splits) < (uint64_t{1} << 32)
+                         ? static_cast<uint32_t>(((uint64_t{1} << 32) + plan.n_splits - 1) / plan.n_splits)
+                         : 0u;
 }
 
 hipError_t launch_gemv_group(int n_planes, int lane_groups, const GemvGroupArgs& args, int total_wg,

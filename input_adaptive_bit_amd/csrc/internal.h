@@ -57,6 +57,10 @@ struct GemvDesc {
     float* acc;
     unsigned* ctrl;
     int d_in, d_out, row_words, chunk, n_splits, n_tiles, wg_begin, x_dtype, y_dtype;
+    // ceil(2^32 / n_splits): the tile of local item a is the high word of
+    // a * split_magic (exact while a * n_splits < 2^32); 0 where that does not
+    // hold for every item, or for one split (the kernel then divides)
+    uint32_t split_magic;
 };
 
 constexpr int kMaxGroup = 8;

@@ -44,6 +44,9 @@ class DeviceLinear:
         import input_adaptive_bit_amd as G
         import torch
         self.b_max = b_max
+        self.q_np = None if q is None else np.asarray(q, np.uint8)
+        self.s_np = np.asarray(s, np.float16)
+        self.z_np = np.asarray(z, np.float16)
         self.q_dev = q_dev if q_dev is not None else to_dev(q, dev)
         self.d_out, self.d_in = self.q_dev.shape
         self.L, self.planes = G.pack(self.q_dev, b_max)

@@ -2,8 +2,9 @@
 
 Bit-exact: packed planes, b_i, the ascending active list and its length,
 the decoded codes.  Within tolerance (max relative error, denominator
-max(|y*_j|, 1e-2 * rms(y*))): fp32 y <= 2e-3; bf16 y <= 2e-3 + 2^-8 and equal
-to the fp32 result rounded to nearest even.  Oracle inputs are the seeded
+max(|y*_j|, 1e-2 * rms(y*))): fp32 y <= 2e-3; bf16 y <= 2e-3 + 2^-8 and, for
+every output, the fp32 result rounded to nearest even (either neighbour only
+within the fp32 results' call-to-call spread of a rounding boundary).  Oracle inputs are the seeded
 synthetic arrays; no expected value comes from the HIP path.
 """
 
@@ -72,14 +73,34 @@ def _run_and_check(dl, x_f32, x_dtype, theta, y_ref, what, dev, check_bf16=True)
         yb = dl.gemv(xd, td, torch.bfloat16)
         torch.cuda.synchronize()
         _check_y(yb, y_ref, TOL_BF16, what + " bf16")
-        # bf16 output is the fp32 result rounded to nearest even; the fp32 values
-        # of two calls may differ in the last bits, so allow one bf16 step
-        rne = O.round_to_bf16(y.astype(np.float32))
+        # bf16 output is the fp32 result rounded to nearest even.  The slices
+        # are added in whatever order they arrive, so the fp32 value of this
+        # call may differ from y in its last bits, by at most the fp32
+        # rounding of its sums.  At the launch shapes of these cases (slices
+        # of at least 64 channels, so at most 64 channels per worker and 64
+        # slices) no chain of additions is 128 long, and each addition is off
+        # by at most 2^-24 of the output's term magnitude
+        # M_j = sum_i |x_i| (|s_j| (code_ij + phi_i) + |z_j|) over loaded
+        # channels, so two calls differ by at most 2^-16 M_j.  Every output
+        # must lie between the RNE roundings of y - delta and y + delta, with
+        # delta that bound plus the spread seen between the two fp32 calls.
+        # M_j is often hundreds of times |y_j| (the phi and z terms cancel), so
+        # that bound is loose; the outputs whose rounding actually flips are
+        # few, and at most 1% may differ from the RNE rounding of y itself.
+        # (With one slice the result is deterministic and the check is exact:
+        # test_gemv_bf16_is_rne_with_one_slice; the exact-integer tests pin
+        # it at every slice count.)
         got = yb.view(torch.int16).cpu().numpy().view(np.uint16)
-        gotf = yb.float().cpu().numpy().astype(np.float64)
-        floor = 1e-2 * float(np.sqrt(np.mean(y ** 2))) if y.size else 0.0
-        assert np.all(np.abs(gotf - y) <= 2.0 ** -8 * np.maximum(np.abs(y), floor) + 1e-30), \
-            f"{what}: bf16 output is not the rounded fp32 output"
+        gotf = S.bf16_bits_to_f32(got).astype(np.float64)
+        x_seen = x_f32 if x_dtype == "f32" else S.bf16_bits_to_f32(S.f32_to_bf16_bits(np.asarray(x_f32, np.float32)))
+        mag = C.gemv(np.abs(np.asarray(x_seen, np.float32)), theta, dl.q_np, np.abs(dl.s_np), np.abs(dl.z_np),
+                     dl.b_max)
+        delta = 4.0 * np.abs(y2 - y) + 2.0 ** -16 * mag
+        lo = S.bf16_bits_to_f32(O.round_to_bf16((y - delta).astype(np.float32))).astype(np.float64)
+        hi = S.bf16_bits_to_f32(O.round_to_bf16((y + delta).astype(np.float32))).astype(np.float64)
+        ok = (gotf >= lo) & (gotf <= hi)
+        assert np.all(ok), f"{what}: bf16 output is not RNE of the fp32 output at {np.flatnonzero(~ok)[:8]}"
+        rne = O.round_to_bf16(y.astype(np.float32))
         assert np.mean(got == rne) >= 0.99, f"{what}: bf16 output is not RNE of the fp32 output"
     return y
 
@@ -171,6 +192,38 @@ def test_gemv_small_case(dev):
     dl = DeviceLinear(L.q, L.s, L.z, 8, dev)
     y_ref = O.gemv(L.x, L.theta, L.q, L.s, L.z, 8, exact=True)
     _run_and_check(dl, L.x, "f32", L.theta, y_ref, "small case", dev)
+
+
+@pytest.mark.parametrize("b_max", [2, 4, 6, 8])
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+def test_gemv_bf16_is_rne_with_one_slice(dev, forced_shape, b_max, x_dtype):
+    """With one slice per tile (d_in <= 256 at the longest slice) each tile's
+    sums are one fixed-order LDS reduction and one add to zero, so the fp32
+    result is the same on every call and the bf16 output must be its RNE
+    rounding at every output."""
+    import torch
+    forced_shape(0, 256)
+    rng = np.random.default_rng(900 + b_max)
+    for d_in, d_out in [(1, 65), (100, 1000), (256, 4100)]:
+        say(f"bf16 one slice b_max={b_max} {d_in}->{d_out} x={x_dtype}")
+        q = rng.integers(0, 1 << b_max, size=(d_out, d_in), dtype=np.uint8)
+        s = rng.uniform(0.001, 0.01, d_out).astype(np.float16)
+        z = rng.normal(0, 0.01, d_out).astype(np.float16)
+        x = rng.standard_t(3, d_in).astype(np.float32)
+        if x_dtype == "bf16":
+            x = S.bf16_bits_to_f32(S.f32_to_bf16_bits(x))
+        theta = np.sort(np.quantile(np.abs(x), np.linspace(0.2, 0.9, b_max // 2))).astype(np.float32)
+        dl = DeviceLinear(q, s, z, b_max, dev)
+        xd, td = to_dev_x(x, x_dtype, dev), _theta_dev(theta, dev)
+        y1 = dl.gemv(xd, td, torch.float32)
+        y2 = dl.gemv(xd, td, torch.float32)
+        yb = dl.gemv(xd, td, torch.bfloat16)
+        torch.cuda.synchronize()
+        y1n = y1.cpu().numpy()
+        _check_y(y1, C.gemv(x, theta, q, s, z, b_max), TOL_F32, "one slice fp32")
+        assert np.array_equal(y1n.view(np.uint32), y2.cpu().numpy().view(np.uint32)), "one slice: calls differ"
+        got = yb.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, O.round_to_bf16(y1n)), "one slice: bf16 output is not RNE of the fp32 output"
 
 
 @pytest.mark.parametrize("b_max", [2, 4, 6, 8])
