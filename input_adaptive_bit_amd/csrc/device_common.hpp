@@ -20,14 +20,6 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
-}
-
 // x_i as fp32 (bf16 widens exactly).  dtype: 0 = bf16, 1 = f32.
 __device__ __forceinline__ float load_x(const void* x, int dtype, int i) {
     if (dtype == 0) return bf16_to_f32(static_cast<const uint16_t*>(x)[i]);

@@ -110,7 +110,23 @@ __device__ __forceinline__ void accumulate(float (&acc)[16 * V], const uint32_t 
     }
 }
 
-static_assert(kWaves == 4, "one count byte per wave in a word");
+static_assert(kWaves == 4, "the prologue sums the bucket counts of four waves");
+
+// Exponents of the slice-list multipliers x_i * 4^(P - Pi) * folded_unit<Pi>(),
+// one byte per plane count Pi = 1 .. 4 (byte Pi - 1).
+template <int P>
+constexpr uint32_t scale_exponents() {
+    uint32_t e = 0;
+    for (int pi = 1; pi <= 4; ++pi) {
+        const int unit_exp = pi == 1 ? 1 : pi == 2 ? 9 : 0;   // log2 of folded_unit<Pi>()
+        const int ex = pi <= P ? 2 * (P - pi) + unit_exp : 0;
+        e |= static_cast<uint32_t>(ex) << (8 * (pi - 1));
+    }
+    return e;
+}
+static_assert(folded_unit<1>() == 2.f && folded_unit<2>() == 512.f && folded_unit<3>() == 1.f &&
+                  folded_unit<4>() == 1.f,
+              "scale_exponents matches the folded units");
 
 // Entries read past a bucket's end: fewer than one batch (U * stride <= 192)
 // beyond the last list entry.  The slice lists are padded so that those
@@ -120,7 +136,7 @@ constexpr int kListPad = 192;
 struct SliceLists {
     uint32_t off[kMaxChunk + kListPad];   // byte offset of the channel's plane 0 row: i * P * row_bytes
     float xv[kMaxChunk + kListPad];       // x_i * 4^(P - Pi) * folded_unit<Pi>(): multiplier of its Pi-plane code
-    uint32_t cnt[4];           // word l, byte w: loaded channels of wave w with l + 1 planes
+    uint32_t cnt[kWaves];      // word w, byte l: loaded channels of wave w with l + 1 planes
     float red_s[kWaves], red_c[kWaves];
     int is_last;               // this workgroup arrived last at its tile
     float S;                   // the tile's sum of x over loaded channels (last arriver)
@@ -305,24 +321,34 @@ __device__ __forceinline__ void gemv_item(const GemvDesc& D, int item) {
     }
     // (with theta_0 <= 0 a zero x would get bits: threads past the slice get none)
     const int pi = mine ? bits_of<P>(xv, th) >> 1 : 0;
+    // Rank of the lane's channel among the wave's channels with the same
+    // plane count (mbcnt: set bits of the ballot below this lane), and the
+    // wave's counts per plane count, one byte each, in one LDS word.
     int rank = 0;
+    uint32_t counts = 0;
 #pragma unroll
     for (int l = 0; l < P; ++l) {
         const unsigned long long m = __ballot(pi == l + 1);
-        if (pi == l + 1) rank = __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == 0) reinterpret_cast<uint8_t*>(L.cnt)[4 * l + wv] = static_cast<uint8_t>(__popcll(m));
+        const int below_lane = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+            static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+        rank = pi == l + 1 ? below_lane : rank;
+        counts |= static_cast<uint32_t>(__popcll(m)) << (8 * l);
     }
+    if (lane == 0) L.cnt[wv] = counts;
     __syncthreads();
     // Bucket bounds and this wave's place in each bucket, as wave-uniform
     // scalars: bucket Pi = 1 first, each in wave then lane order.
     int start[5];   // bucket Pi holds entries start[Pi - 1] .. start[Pi] - 1
     int below[4];   // first entry of bucket l + 1 written by this wave
+    uint32_t cw[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) cw[w] = __builtin_amdgcn_readfirstlane(L.cnt[w]);
     start[0] = 0;
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
         if (l < P) {
-            const uint32_t c = __builtin_amdgcn_readfirstlane(L.cnt[l]);
-            const int c0 = c & 255, c1 = (c >> 8) & 255, c2 = (c >> 16) & 255, c3 = c >> 24;
+            const int c0 = (cw[0] >> (8 * l)) & 255, c1 = (cw[1] >> (8 * l)) & 255;
+            const int c2 = (cw[2] >> (8 * l)) & 255, c3 = (cw[3] >> (8 * l)) & 255;
             below[l] = start[l] + (wv > 0 ? c0 : 0) + (wv > 1 ? c1 : 0) + (wv > 2 ? c2 : 0);
             start[l + 1] = start[l] + c0 + c1 + c2 + c3;
         } else {
@@ -336,8 +362,10 @@ __device__ __forceinline__ void gemv_item(const GemvDesc& D, int item) {
         for (int l = 1; l < P; ++l) pos = pi == l + 1 ? below[l] : pos;
         pos += rank;
         L.off[pos] = static_cast<uint32_t>(i0 + tid) * (P * static_cast<uint32_t>(D.row_words) * 4u);
-        const float unit = pi == 1 ? folded_unit<1>() : pi == 2 ? folded_unit<2>() : 1.f;
-        L.xv[pos] = xv * (static_cast<float>(1u << (2 * (P - pi))) * unit);
+        // x_i * 4^(P - Pi) * folded_unit<Pi>() as one exponent step: the
+        // power of two for Pi = 1 .. 4 is byte Pi - 1 of kScaleExp.
+        constexpr uint32_t kScaleExp = scale_exponents<P>();
+        L.xv[pos] = __builtin_ldexpf(xv, static_cast<int>((kScaleExp >> (8 * (pi - 1))) & 255u));
     }
     __syncthreads();
 
@@ -483,7 +511,7 @@ __device__ __forceinline__ void gemv_item(const GemvDesc& D, int item) {
             if (D.y_dtype == GRINQH_F32)
                 static_cast<float*>(D.y)[j] = yv;
             else
-                static_cast<uint16_t*>(D.y)[j] = f32_to_bf16_rne(yv);
+                static_cast<uint16_t*>(D.y)[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(yv));   // RNE
         }
     }
 }
