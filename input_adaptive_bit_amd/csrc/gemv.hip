@@ -256,13 +256,13 @@ struct Bucket {
     __device__ __forceinline__ void finish(float (&acc)[16 * V], const SliceLists& L, int group,
                                            const PlaneSrc& src) {
         compute_batch<P, Pb, V, U, stride, true>(acc, B, &L.xv[ew + group], group, end - ew);
-        // Later batches exist only for buckets longer than one batch.  The
-        // four-plane ones (every channel in dense mode) decode every slot of
-        // them, so that both channels of a batch stay in flight together; the
+        // Later batches exist only for buckets longer than one batch.  Those
+        // of the top bucket (Pb = P: every channel in dense mode) decode every
+        // slot, so that the channels of a batch stay in flight together; the
         // empty slots of a bucket's last batch cost little next to the rest.
         for (ew += stride * U; ew < end; ew += stride * U) {
             load_batch<P, Pb, V, U, stride>(B, &L.off[ew + group], group, end - ew, src);
-            compute_batch<P, Pb, V, U, stride, (Pb < 4)>(acc, B, &L.xv[ew + group], group, end - ew);
+            compute_batch<P, Pb, V, U, stride, (Pb < P)>(acc, B, &L.xv[ew + group], group, end - ew);
         }
     }
 };
