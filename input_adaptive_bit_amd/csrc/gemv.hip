@@ -192,10 +192,11 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 // The lists are read at a per-lane base and compile-time offsets u * stride,
 // so an entry costs no address arithmetic; validity is one compare of the
 // lane group against the wave-uniform number of entries left.  All U list
-// entries are read first, whether valid or not (the lists are padded), and
-// an invalid entry's base is pushed past the buffer by adding 2^31: the
-// value read is used on every path, so the reads are not put behind
-// branches one by one, each waiting for its own LDS round trip.
+// entries are read first, whether valid or not (the lists are padded), so
+// that the reads are not put behind branches one by one, each waiting for
+// its own LDS round trip; an invalid entry's base is then replaced by
+// kOutOfRange with a select.  (An entry past the slice's last channel holds
+// whatever the LDS held before, so its value must not reach the address.)
 template <int P, int Pb, int V, int U, int stride>
 __device__ __forceinline__ void load_batch(Batch<Pb, V, U>& B, const uint32_t* offp, int group, int left,
                                            const PlaneSrc& src) {
@@ -205,8 +206,7 @@ __device__ __forceinline__ void load_batch(Batch<Pb, V, U>& B, const uint32_t* o
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const bool ok = group < left - u * stride;
-        // o + lane_bytes < 2^31 for a valid entry's row (planes < 2 GiB)
-        const uint32_t base = o[u] + src.lane_bytes + (ok ? 0u : kOutOfRange);
+        const uint32_t base = ok ? o[u] + src.lane_bytes : kOutOfRange;
 #pragma unroll
         for (int p = 0; p < Pb; ++p)
             load_words<V>(src.rsrc, base, static_cast<uint32_t>(p) * src.row_bytes, B.w[u][p]);
