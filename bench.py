@@ -58,6 +58,7 @@ MALL_BYTES = 256 << 20
 KERNEL_SOURCES = ("input_adaptive_bit_amd/csrc/gemv.hip", "input_adaptive_bit_amd/csrc/decode.hpp",
                   "input_adaptive_bit_amd/csrc/device_common.hpp", "input_adaptive_bit_amd/csrc/internal.h")
 COUNTER_SUMMARY = "profiles/gemv_one_kernel__8b_decode_linears_e3__hbm_counters.md"
+SQ_SUMMARY = "profiles/gemv_one_kernel__8b_decode_linears_e3__sq_counters.md"
 
 
 def log(*a):
@@ -77,23 +78,30 @@ def kernel_sources_hash() -> str:
     return h.hexdigest()
 
 
-def counted_traffic(eff: int):
-    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary
-    (scaled by a copy kernel of known size), or None when that summary was
-    taken on other kernel sources or another workload."""
+def counted_field(path: str, field: str, eff: int):
+    """A per-launch figure from a committed counter summary, or None when that
+    summary was taken on other kernel sources or another workload."""
     if eff != 3:
         return None
     try:
-        with open(os.path.join(ROOT, COUNTER_SUMMARY)) as fh:
+        with open(os.path.join(ROOT, path)) as fh:
             text = fh.read()
     except OSError:
         return None
-    fields = dict(line.split(": ", 1) for line in text.splitlines() if line.startswith(("traffic_", "kernel_")))
+    fields = dict(line.split(": ", 1) for line in text.splitlines()
+                  if line.startswith(("traffic_", "kernel_", "valu_")))
     if fields.get("kernel_sources_sha256", "").strip() != kernel_sources_hash():
         return None
-    if fields.get("traffic_workload", "").strip() != "per-call":
+    if fields.get("traffic_workload", "").strip() != "per-call" or field not in fields:
         return None
-    return int(float(fields["traffic_bytes_per_launch"]))
+    return float(fields[field])
+
+
+def counted_traffic(eff: int):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary
+    (scaled by a copy kernel of known size), or None (see counted_field)."""
+    v = counted_field(COUNTER_SUMMARY, "traffic_bytes_per_launch", eff)
+    return None if v is None else int(v)
 
 
 def fit_line(xs, ys):
@@ -667,6 +675,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": counted_traffic(eff),
+            # share of the dispatch's SIMD cycles issuing VALU work (SQ counters; None as for traffic)
+            "valu_issue_share": counted_field(SQ_SUMMARY, "valu_issue_share_per_launch", eff),
             "kernel": "gemv_one_kernel (three grinqh_gemv launches per step; per-launch average)",
             "avg_launch_us": round(avg_launch_us, 3),
             "bytes_per_launch": int(bytes_per_launch),

@@ -51,3 +51,18 @@ def test_fit_line_recovers_a_line():
     import bench
     a, b = bench.fit_line([2, 3, 4, 8], [10.0 + 2 * 1.5, 10.0 + 3 * 1.5, 10.0 + 4 * 1.5, 10.0 + 8 * 1.5])
     assert abs(a - 10.0) < 1e-9 and abs(b - 1.5) < 1e-9
+
+
+def test_committed_counter_summaries_match_the_kernel_sources():
+    """The HBM and SQ counter summaries under profiles/ were taken on the
+    kernel sources as they stand (their recorded sha256 matches), so the
+    bench line carries their traffic and VALU figures instead of null."""
+    sys.path.insert(0, ROOT)
+    import bench
+    traffic = bench.counted_traffic(3)
+    share = bench.counted_field(bench.SQ_SUMMARY, "valu_issue_share_per_launch", 3)
+    assert traffic is not None and share is not None
+    # the counted traffic is the required bytes plus the split-K adds: close to 1x
+    assert 1.0 <= traffic / (50214912 / 3) < 1.2
+    assert 0.0 < share < 1.0
+    assert bench.counted_traffic(8) is None
