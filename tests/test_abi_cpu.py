@@ -267,3 +267,20 @@ def test_force_launch_argument_checks():
         assert lib.grinqh_debug_force_launch(*bad) == 1, bad   # GRINQH_EINVAL
     for good in [(1, 7, 1), (8, 256, 3), (2, 64, 2), (0, 0, 0)]:
         assert lib.grinqh_debug_force_launch(*good) == 0, good   # GRINQH_OK
+
+
+def test_multiply_high_tile_split_is_exact_where_the_host_uses_it():
+    """The GEMV takes a workgroup's tile as the high word of item * m with
+    m = ceil(2^32 / n_splits), and the host uses that only while
+    n_tiles * n_splits * n_splits < 2^32 (otherwise the kernel divides).
+    Within that bound the quotient is exact: checked at the bound's edges
+    and on random items for many slice counts."""
+    import numpy as np
+    rng = np.random.default_rng(5)
+    for n in list(range(2, 300)) + [1023, 4096, 4097, 16383, 65535]:
+        m = ((1 << 32) + n - 1) // n
+        n_items_max = ((1 << 32) - 1) // n          # items * n < 2^32
+        a = np.concatenate([np.arange(min(n_items_max, 3 * n)), rng.integers(0, n_items_max, 2000),
+                            [n_items_max - 1]]).astype(np.uint64)
+        q = (a * np.uint64(m)) >> np.uint64(32)
+        assert np.array_equal(q, a // np.uint64(n)), n

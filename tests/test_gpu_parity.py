@@ -245,6 +245,28 @@ def test_gemv_ragged_shapes(dev, b_max, d_in, d_out, x_dtype):
     _run_and_check(dl, x, x_dtype, theta, y_ref, f"{d_in}->{d_out} b{b_max}", dev)
 
 
+@pytest.mark.parametrize("d_in,d_out", [(66000, 100), (3000, 5000)])
+def test_gemv_one_channel_slices(dev, forced_shape, d_in, d_out):
+    """Slices of one channel: every input channel is its own workgroup.  At
+    66000 channels the item count times the slice count passes 2^32, so the
+    kernel takes a workgroup's tile by integer division instead of the
+    host's multiply-high reciprocal; at 3000 x 5000 (20 tiles) it uses the
+    reciprocal over 60000 items."""
+    import torch
+    forced_shape(8, 1)
+    rng = np.random.default_rng(d_in + d_out)
+    q = rng.integers(0, 256, size=(d_out, d_in), dtype=np.uint8)
+    s = rng.uniform(0.001, 0.01, d_out).astype(np.float16)
+    z = rng.normal(0, 0.01, d_out).astype(np.float16)
+    x = S.bf16_bits_to_f32(S.f32_to_bf16_bits(rng.standard_t(3, d_in).astype(np.float32)))
+    theta = np.sort(np.quantile(np.abs(x), np.linspace(0.2, 0.9, 4))).astype(np.float32)
+    say(f"one-channel slices {d_in}->{d_out}")
+    dl = DeviceLinear(q, s, z, 8, dev)
+    y = dl.gemv(to_dev_x(x, "bf16", dev), _theta_dev(theta, dev), torch.float32)
+    torch.cuda.synchronize()
+    _check_y(y, C.gemv(x, theta, q, s, z, 8), TOL_F32, f"one-channel slices {d_in}->{d_out}")
+
+
 @pytest.mark.parametrize("lane_groups", [1, 2, 4, 8])
 @pytest.mark.parametrize("chunk", [7, 64, 256])
 @pytest.mark.parametrize("b_max", [8, 4])
