@@ -5,7 +5,7 @@
 // to 256 input channels); one 256-thread workgroup per item, all items
 // resident at once (one generation of workgroups).  Slices are as long as
 // the prologue allows, and the tile width (lane groups per wave) follows the
-// launch's workgroup count (plan_gemv, choose_lane_groups).
+// launch's workgroup count (plan_gemv, search_launch).
 //
 // Prologue (key design 1).  The workgroup reads its slice of x, assigns
 // b_i = 2 * #{k : theta_k <= |x_i|} with exact fp32 compares and bucket-sorts
@@ -233,12 +233,14 @@ __device__ __forceinline__ void compute_batch(float (&acc)[16 * V], const Batch<
 // Channels in flight per worker and bucket: the first batch of every bucket
 // is issued before any decoding starts, and a batch holds a typical slice's
 // share of its bucket, so a workgroup waits for about one memory round trip.
-template <int Pb>
-struct BatchSize { static constexpr int U = Pb == 4 ? 2 : Pb == 3 ? 3 : Pb == 2 ? 5 : 6; };
+// At b_max 2 (P = 1) every loaded channel is in the one bucket, whose later
+// batches decode every slot; six channels there spill registers, four do not.
+template <int P, int Pb>
+struct BatchSize { static constexpr int U = P == 1 ? 4 : Pb == 4 ? 2 : Pb == 3 ? 3 : Pb == 2 ? 5 : 6; };
 
 template <int P, int Pb, int V, int G>
 struct Bucket {
-    static constexpr int U = BatchSize<Pb>::U;
+    static constexpr int U = BatchSize<P, Pb>::U;
     static constexpr int stride = kWaves * G;
     static_assert(U * stride <= kListPad, "list padding covers a batch past the end");
     Batch<Pb, V, U> B;
