@@ -61,6 +61,20 @@ COUNTER_SUMMARY = "profiles/gemv_one_kernel__8b_decode_linears_e3__hbm_counters.
 SQ_SUMMARY = "profiles/gemv_one_kernel__8b_decode_linears_e3__sq_counters.md"
 
 
+# What the pages report for this path (GRINQH note, papernotes.org, the
+# hardware throughput and ablation table; and the summary page's key
+# results), restated: model-level decode throughput on one RTX 4090, not a
+# kernel figure and not comparable with this GPU's numbers.
+PAGES_CONTEXT = {
+    "hardware": "1x NVIDIA RTX 4090 (custom Triton GEMV, 8B model)",
+    "decode_tok_per_s": {"GPTQ 4-bit MARLIN": 160.4, "GRINQH b_max 8, 4 eff. bits": 157.6,
+                         "GRINQH b_max 8, 3 eff. bits": 182.2, "GRINQH b_max 8, 2 eff. bits": 204.6},
+    "claims": ["decode up to 1.28x the tokens/s of 4-bit MARLIN (at 2 effective bits)",
+               "latency scaling in proportion to the effective bits"],
+    "use": "context only",
+}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -194,26 +208,33 @@ class DecodeStep:
     each with its own activations and thresholds; codes drawn on the device
     from seeded generators (7.0 GB of planes at b_max 8)."""
 
-    def __init__(self, dev, effs, n_layers=32):
+    def __init__(self, dev, effs, n_layers=32, unfused=False):
         import torch
         import input_adaptive_bit_amd as G
         import synthetic as S
-        specs = S.llama8b_decode_step(3, n_layers)
+        if unfused:
+            # the seven linears of a layer as separate launches; q, k and v
+            # (and gate and up) read the same x and thresholds
+            pairs = S.llama8b_decode_step_unfused(3, n_layers)
+        else:
+            pairs = [(spec, spec.key) for spec in S.llama8b_decode_step(3, n_layers)]
         self.ops = []
         self.req = {e: 0.0 for e in effs}
-        for spec in specs:
+        inputs = {}
+        for spec, in_key in pairs:
             g = torch.Generator(device=dev)
             g.manual_seed(S.torch_seed(spec.key, 0))
             q = torch.randint(0, 256, (spec.d_out, spec.d_in), generator=g, dtype=torch.uint8, device=dev)
             L, planes = G.pack(q, 8)
             del q
-            xs, _ = S.gen_x_stream(spec)
             s_np, z_np = S.gen_scales(spec)
-            x = torch.from_numpy(S.f32_to_bf16_bits(xs[spec.n_calib]).view(np.int16).copy()).to(dev)
-            th = {}
+            if in_key not in inputs:
+                xs, _ = S.gen_x_stream(spec)
+                x = torch.from_numpy(S.f32_to_bf16_bits(xs[spec.n_calib]).view(np.int16).copy()).to(dev)
+                inputs[in_key] = (x, {e: torch.from_numpy(S.calibrate_theta(xs[:spec.n_calib], S.QUANTILES_B8[e], 4)).to(dev)
+                                      for e in effs})
+            x, th = inputs[in_key]
             for e in effs:
-                t = S.calibrate_theta(xs[:spec.n_calib], S.QUANTILES_B8[e], 4)
-                th[e] = torch.from_numpy(t).to(dev)
                 bits, _, _ = G.assign_bits(L, x.view(torch.bfloat16), th[e])
                 self.req[e] += required_bytes(bits.cpu().numpy(), spec.d_out)
             self.ops.append(dict(L=L, planes=planes, x=x.view(torch.bfloat16), th=th,
@@ -617,7 +638,7 @@ def main() -> int:
             log(f"prefill {M}x{di}->{do} b_max {bm}: {t:.1f} us, {flops / t / 1e6:.1f} TFLOP/s; "
                 f"torch bf16 dense {tt:.1f} us")
 
-    decode_step, decode_fit = {}, {}
+    decode_step, decode_fit, decode_step_unfused = {}, {}, {}
     if not args.no_decode_step:
         for sh in shapes:
             sh.planes = sh.planes[:1]
@@ -636,6 +657,19 @@ def main() -> int:
         a, b = fit_line([v["required_GB"] for v in decode_step.values()], [v["us"] for v in decode_step.values()])
         decode_fit = {"intercept_us": round(a, 1), "intercept_us_per_launch": round(a / len(ds.ops), 3),
                       "marginal_GB/s": round(1e3 / b, 1) if b > 0 else None}
+        del ds
+        torch.cuda.empty_cache()
+        # the same step with the seven linears of a layer launched one by one
+        # (224 launches), as the layer is written; at ~3 bits and dense
+        ds = DecodeStep(dev, [3, 8], unfused=True)
+        for e in (3, 8):
+            t = time_per_rep(lambda r, e=e: ds.launch(e), 4)
+            gbs = ds.req[e] / (t * 1e-6) / 1e9
+            decode_step_unfused[str(e) if e != 8 else "8 (dense)"] = {
+                "us": round(t, 2), "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "required_GB": round(ds.req[e] / 1e9, 4), "launches": len(ds.ops),
+                "us_per_launch": round(t / len(ds.ops), 3)}
+            log(f"decode step, seven launches per layer, eff {e}: {t:.1f} us, {gbs:.1f} GB/s")
         del ds
         torch.cuda.empty_cache()
 
@@ -692,6 +726,8 @@ def main() -> int:
         "rtn_quantisation_b_max_8": rtn,
         "decode_step_32_layers": decode_step,
         "decode_step_fit_us_vs_GB": decode_fit,
+        "decode_step_32_layers_seven_launches_per_layer": decode_step_unfused,
+        "pages_context": PAGES_CONTEXT,
         "prefill_gemm": prefill,
     }
     print(json.dumps(out), flush=True)

@@ -33,7 +33,8 @@ __all__ = [
     "rng_for", "f32_to_bf16_bits", "bf16_bits_to_f32", "fp16_bits",
     "gen_codes", "gen_scales", "gen_x_stream", "calibrate_theta", "make_linear",
     "small_case", "llama8b_linears", "llama8b_linears_b6", "llama8b_linears_b4", "llama8b_decode_step",
-    "llama70b_linears", "LLAMA8B_SHAPES", "LLAMA8B_FUSED_LAYER", "LLAMA70B_SHAPES",
+    "llama70b_linears", "LLAMA8B_SHAPES", "LLAMA8B_FUSED_LAYER", "LLAMA8B_LAYER_UNFUSED", "LLAMA70B_SHAPES",
+    "llama8b_decode_step_unfused",
     "torch_seed",
 ]
 
@@ -66,6 +67,10 @@ LLAMA8B_SHAPES = ((4096, 4096), (4096, 14336), (14336, 4096))
 # o needs the attention output and down the activated gate|up output, so the
 # four run one after another
 LLAMA8B_FUSED_LAYER = ((4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096))
+# the same layer as its seven separate linears (d_in, d_out, input group): q, k and
+# v share one input, gate and up another
+LLAMA8B_LAYER_UNFUSED = ((4096, 4096, 0), (4096, 1024, 0), (4096, 1024, 0), (4096, 4096, 1),
+                         (4096, 14336, 2), (4096, 14336, 2), (14336, 4096, 3))
 LLAMA70B_SHAPES = ((8192, 8192), (8192, 28672), (28672, 8192))
 
 
@@ -220,6 +225,19 @@ def llama8b_decode_step(eff_bits: int, n_layers: int = 32) -> list:
         for lin, (di, do) in enumerate(LLAMA8B_FUSED_LAYER):
             out.append(LinearSpec(di, do, 8, "t3", "bf16", QUANTILES_B8[eff_bits],
                                   key=(4, 1, layer, lin)))
+    return out
+
+
+def llama8b_decode_step_unfused(eff_bits: int, n_layers: int = 32) -> list:
+    """The seven linears of every decoder layer as separate launches, in
+    order (q, k, v, o, gate, up, down): (spec, input key) pairs, where
+    linears of one layer with the same input key read the same x and
+    thresholds (those of the first of them)."""
+    out = []
+    for layer in range(n_layers):
+        for lin, (di, do, grp) in enumerate(LLAMA8B_LAYER_UNFUSED):
+            out.append((LinearSpec(di, do, 8, "t3", "bf16", QUANTILES_B8[eff_bits], key=(4, 3, layer, lin)),
+                        (layer, grp)))
     return out
 
 
