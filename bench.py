@@ -439,6 +439,9 @@ def main() -> int:
     ap.add_argument("--no-70b", action="store_true", help="skip the 70B shapes (4.3 GB of planes)")
     ap.add_argument("--no-decode-step", action="store_true",
                     help="skip the 32-layer decode-step measurement (7.0 GB of planes)")
+    ap.add_argument("--decode-effs", default="2,3,4,6,8",
+                    help="effective bits of the 32-layer decode step (comma list; the seven-launch form "
+                         "runs at those of 3 and 8 listed)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-stage GEMM timing")
     ap.add_argument("--no-offline", action="store_true", help="skip calibration and RTN timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -644,7 +647,7 @@ def main() -> int:
             sh.planes = sh.planes[:1]
             sh.n_copies = 1
         torch.cuda.empty_cache()
-        effs_ds = (2, 3, 4, 6, 8)
+        effs_ds = tuple(int(v) for v in args.decode_effs.split(","))
         ds = DecodeStep(dev, list(effs_ds))
         for e in effs_ds:
             t = time_per_rep(lambda r, e=e: ds.launch(e), 4)
@@ -654,15 +657,18 @@ def main() -> int:
                 "required_GB": round(ds.req[e] / 1e9, 4), "launches": len(ds.ops),
                 "us_per_launch": round(t / len(ds.ops), 3)}
             log(f"decode step eff {e}: {t:.1f} us, {gbs:.1f} GB/s")
-        a, b = fit_line([v["required_GB"] for v in decode_step.values()], [v["us"] for v in decode_step.values()])
-        decode_fit = {"intercept_us": round(a, 1), "intercept_us_per_launch": round(a / len(ds.ops), 3),
-                      "marginal_GB/s": round(1e3 / b, 1) if b > 0 else None}
+        if len(effs_ds) >= 2:
+            a, b = fit_line([v["required_GB"] for v in decode_step.values()],
+                            [v["us"] for v in decode_step.values()])
+            decode_fit = {"intercept_us": round(a, 1), "intercept_us_per_launch": round(a / len(ds.ops), 3),
+                          "marginal_GB/s": round(1e3 / b, 1) if b > 0 else None}
         del ds
         torch.cuda.empty_cache()
         # the same step with the seven linears of a layer launched one by one
         # (224 launches), as the layer is written; at ~3 bits and dense
-        ds = DecodeStep(dev, [3, 8], unfused=True)
-        for e in (3, 8):
+        effs_unf = [e for e in (3, 8) if e in effs_ds]
+        ds = DecodeStep(dev, effs_unf, unfused=True) if effs_unf else None
+        for e in effs_unf:
             t = time_per_rep(lambda r, e=e: ds.launch(e), 4)
             gbs = ds.req[e] / (t * 1e-6) / 1e9
             decode_step_unfused[str(e) if e != 8 else "8 (dense)"] = {
