@@ -66,3 +66,20 @@ def test_committed_counter_summaries_match_the_kernel_sources():
     assert 1.0 <= traffic / (50214912 / 3) < 1.2
     assert 0.0 < share < 1.0
     assert bench.counted_traffic(8) is None
+
+
+def test_every_gemv_profile_was_taken_on_the_current_kernel_sources():
+    """Every committed GEMV profile summary names the sha256 of the kernel
+    sources it was taken on, and that is the hash of the sources as they
+    stand: a kernel change without a new profile fails here."""
+    import glob
+    import re
+    sys.path.insert(0, ROOT)
+    import bench
+    files = sorted(glob.glob(os.path.join(ROOT, "profiles", "gemv_one_kernel__*.md")))
+    assert len(files) >= 4
+    for f in files:
+        with open(f) as fh:
+            m = re.search(r"sha256:?\s*([0-9a-f]{64})", fh.read())
+        assert m is not None, f
+        assert m.group(1) == bench.kernel_sources_hash(), f
