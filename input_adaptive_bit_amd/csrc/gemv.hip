@@ -48,7 +48,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxChunk = kThreads;       // one channel per thread in the prologue
-constexpr int kMinChunk = 64;             // shortest slice the launch shape picks by itself
+constexpr int kMinChunk = 128;            // shortest slice the launch shape picks by itself
 constexpr int kWgPerCu = 4;               // resident workgroups per CU the kernel is sized for
 constexpr int kV = 2;                     // plane words per lane per plane row (8-byte loads)
 
@@ -631,7 +631,11 @@ LaunchShape search_launch(const grinqh_layout* layouts, int n, long cus) {
     // unless W is a multiple of the CU count; shorten the slices (not below
     // kMinChunk) until W reaches the next multiple, without passing it.  W
     // does not grow with the slice length, so the shortest slice that stays
-    // within the target is found by bisection.
+    // within the target is found by bisection.  The floor matters only for
+    // layouts with few tiles (d_out of a few thousand), where a slice of 64
+    // channels streams too little to pay for its share of the tile's
+    // hand-off: 4096->1024 took 6.3 us with 64-channel slices on every CU
+    // and 5.8 us with 128-channel slices on half of them.
     const long wmin = launch_workgroups(layouts, n, sh.lane_groups, kMaxChunk);
     const long target = (wmin + cus - 1) / cus * cus;
     int lo = kMinChunk, hi = kMaxChunk;          // W(hi) <= target holds
