@@ -397,36 +397,55 @@ __device__ __forceinline__ void gemv_item(const GemvDesc& D, int item) {
     Bucket<P, (P >= 2 ? 2 : 1), V, G> k2;
     Bucket<P, (P >= 3 ? 3 : 1), V, G> k3;
     Bucket<P, (P >= 4 ? 4 : 1), V, G> k4;
-    // Two buckets in flight at a time: the next bucket's first batch is
-    // issued after the bucket two ahead is decoded.  Every workgroup on a CU
-    // then keeps a part of its loads in the CU's queue instead of all of
-    // them, so the resident workgroups are served side by side rather than
-    // one after another.
-    if constexpr (P >= 4) k4.first(L, start[3], start[4], wv, group, src);
-    if constexpr (P >= 3) k3.first(L, start[2], start[3], wv, group, src);
-    if constexpr (P <= 2) {
-        if constexpr (P >= 2) k2.first(L, start[1], start[2], wv, group, src);
-        k1.first(L, start[0], start[1], wv, group, src);
-    }
-
     // slice sums S and C over loaded channels (fixed-order reduction), while
     // the first plane loads are in flight
-    {
+    auto slice_sums = [&]() {
         const float s_w = wave_sum(pi > 0 ? xv : 0.f);
         const float c_w = wave_sum(pi > 0 ? xv * phi_of(b_max, 2 * pi) : 0.f);
         if (lane == 0) {
             L.red_s[wv] = s_w;
             L.red_c[wv] = c_w;
         }
+    };
+    if (P >= 3 && start[P - 1] == 0) {
+        // Every loaded channel of the slice has all P planes (dense mode, or
+        // thresholds that load no channel partially): only the top bucket is
+        // streamed, and the empty buckets issue no loads at all.  (Their
+        // out-of-range loads would cost the CU's address unit as much as L2
+        // hits: 25 wave-loads per wave at b_max 8.)  A separate path keeps
+        // the wait counts of both exact.  At b_max 4 the empty bucket costs
+        // 6 wave-loads, and the second path would spill registers there.
+        if constexpr (P == 4) {
+            k4.first(L, start[3], start[4], wv, group, src);
+            slice_sums();
+            k4.finish(acc, L, group, src);
+        } else if constexpr (P == 3) {
+            k3.first(L, start[2], start[3], wv, group, src);
+            slice_sums();
+            k3.finish(acc, L, group, src);
+        }
+    } else {
+        // Two buckets in flight at a time: the next bucket's first batch is
+        // issued after the bucket two ahead is decoded.  Every workgroup on
+        // a CU then keeps a part of its loads in the CU's queue instead of
+        // all of them, so the resident workgroups are served side by side
+        // rather than one after another.
+        if constexpr (P >= 4) k4.first(L, start[3], start[4], wv, group, src);
+        if constexpr (P >= 3) k3.first(L, start[2], start[3], wv, group, src);
+        if constexpr (P <= 2) {
+            if constexpr (P >= 2) k2.first(L, start[1], start[2], wv, group, src);
+            k1.first(L, start[0], start[1], wv, group, src);
+        }
+        slice_sums();
+        if constexpr (P >= 4) k4.finish(acc, L, group, src);
+        if constexpr (P >= 3) {
+            k2.first(L, start[1], start[2], wv, group, src);
+            k3.finish(acc, L, group, src);
+            k1.first(L, start[0], start[1], wv, group, src);
+        }
+        if constexpr (P >= 2) k2.finish(acc, L, group, src);
+        k1.finish(acc, L, group, src);
     }
-    if constexpr (P >= 4) k4.finish(acc, L, group, src);
-    if constexpr (P >= 3) {
-        k2.first(L, start[1], start[2], wv, group, src);
-        k3.finish(acc, L, group, src);
-        k1.first(L, start[0], start[1], wv, group, src);
-    }
-    if constexpr (P >= 2) k2.finish(acc, L, group, src);
-    k1.finish(acc, L, group, src);
 
 
     // ---- reduction: every worker stores its partial row to LDS, then each

@@ -604,3 +604,53 @@ def test_gemv_group_of_eight(dev):
             got = o[5].cpu().numpy()
             err = O.max_rel_error(got, ref)
             assert err <= TOL_F32, (rep, k, err, _mismatch(got, ref))
+
+
+@pytest.mark.parametrize("b_max", [6, 8])
+def test_gemv_slices_with_only_full_channels(dev, b_max):
+    """Slices whose loaded channels all take every plane go down their own
+    path (only the top bucket streamed); the other slices of the same launch
+    take the general one.  Small-integer activations with s = z = 1 make the
+    sums exact, so y must equal the oracle exactly: for x whose first half
+    holds only full or skipped channels (both paths in one launch), for x
+    where every slice is full, and for zero thresholds (every channel full),
+    on single calls and on a group launch of the three."""
+    import torch
+    import input_adaptive_bit_amd as G
+    P = b_max // 2
+    rng = np.random.default_rng(400 + b_max)
+    d_in, d_out = 4096 + 77, 2000
+    q = rng.integers(0, 1 << b_max, size=(d_out, d_in), dtype=np.uint8)
+    s = np.ones(d_out, np.float16)
+    z = np.ones(d_out, np.float16)
+    theta = np.arange(1, P + 1, dtype=np.float32)
+    full = np.array([0.0, P, -P, P + 1, -(P + 1)], np.float32)            # 0 bits or b_max
+    mixed = np.array([0.5, 1, -1, 2, -2, 3, -3, 4, -4, 0], np.float32)
+    x_half = np.concatenate([rng.choice(full, d_in // 2), rng.choice(mixed, d_in - d_in // 2)])
+    x_full = rng.choice(full, d_in)
+    x_small = rng.choice(mixed, d_in)
+    cases = [(x_half, theta), (x_full, theta), (x_small, np.zeros(P, np.float32))]
+    dl = DeviceLinear(q, s, z, b_max, dev)
+    say(f"gemv slices with only full channels b_max={b_max}")
+    refs = [C.gemv(x, th, q, s, z, b_max) for x, th in cases]
+    for ref in refs:
+        assert np.max(np.abs(ref)) < 2 ** 23
+    devs = [(to_dev_x(x, "bf16", dev), _theta_dev(th, dev)) for x, th in cases]
+    for rep in range(3):
+        outs = [dl.gemv(xd, td, torch.float32) for xd, td in devs]
+        torch.cuda.synchronize()
+        for k, (y, ref) in enumerate(zip(outs, refs)):
+            got = y.cpu().numpy().astype(np.float64)
+            assert np.array_equal(got, ref), (rep, k, int(np.sum(got != ref)))
+    layouts = [dl.L] * 3
+    ys = [torch.empty(d_out, dtype=torch.float32, device=dev) for _ in cases]
+    ops = [(xd, td, dl.planes, dl.s, dl.z, y) for (xd, td), y in zip(devs, ys)]
+    ws = G.new_group_workspace(layouts, dev)
+    for rep in range(2):
+        for y in ys:
+            y.fill_(float("nan"))
+        G.grinqh_gemv_group(layouts, ops, ws)
+        torch.cuda.synchronize()
+        for k, (y, ref) in enumerate(zip(ys, refs)):
+            got = y.cpu().numpy().astype(np.float64)
+            assert np.array_equal(got, ref), ("group", rep, k, int(np.sum(got != ref)))
