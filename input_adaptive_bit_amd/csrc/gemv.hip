@@ -434,7 +434,10 @@ __device__ __forceinline__ void gemv_item(const GemvDesc& D, int item) {
         if constexpr (P >= 3) k3.first(L, start[2], start[3], wv, group, src);
         if constexpr (P <= 2) {
             if constexpr (P >= 2) k2.first(L, start[1], start[2], wv, group, src);
-            k1.first(L, start[0], start[1], wv, group, src);
+            // the last batch issued: when its bucket is empty (dense mode at
+            // b_max 4) it issues nothing, and the waits of the decode before
+            // it only gain loads that left at the same time
+            if (P == 1 || start[1] > start[0]) k1.first(L, start[0], start[1], wv, group, src);
         }
         slice_sums();
         if constexpr (P >= 4) k4.finish(acc, L, group, src);
