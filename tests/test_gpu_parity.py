@@ -654,3 +654,33 @@ def test_gemv_slices_with_only_full_channels(dev, b_max):
         for k, (y, ref) in enumerate(zip(ys, refs)):
             got = y.cpu().numpy().astype(np.float64)
             assert np.array_equal(got, ref), ("group", rep, k, int(np.sum(got != ref)))
+
+
+@pytest.mark.parametrize("lane_groups", [1, 2, 4, 8])
+def test_gemv_full_channel_slices_at_every_tile_width(dev, forced_shape, lane_groups):
+    """The path of slices whose loaded channels all take every plane, at each
+    tile width and with short slices (96 channels, so the top bucket needs
+    several batches and a ragged last one): exact integer sums against the
+    oracle at b_max 8 and 6, with half the slices on that path and half on the
+    general one."""
+    import torch
+    d_in, d_out = 1000, 777
+    forced_shape(lane_groups, 96)
+    for b_max in (8, 6):
+        P = b_max // 2
+        rng = np.random.default_rng(500 + 10 * lane_groups + b_max)
+        q = rng.integers(0, 1 << b_max, size=(d_out, d_in), dtype=np.uint8)
+        s = np.ones(d_out, np.float16)
+        z = np.ones(d_out, np.float16)
+        theta = np.arange(1, P + 1, dtype=np.float32)
+        full = np.array([0.0, P, -P, P + 1, -(P + 1)], np.float32)
+        mixed = np.array([0.5, 1, -1, 2, -2, 3, -3, 4, -4, 0], np.float32)
+        x = np.concatenate([rng.choice(full, d_in // 2), rng.choice(mixed, d_in - d_in // 2)])
+        dl = DeviceLinear(q, s, z, b_max, dev)
+        say(f"full-channel slices G={lane_groups} b_max={b_max}")
+        ref = C.gemv(x, theta, q, s, z, b_max)
+        assert np.max(np.abs(ref)) < 2 ** 23
+        y = dl.gemv(to_dev_x(x, "bf16", dev), _theta_dev(theta, dev), torch.float32)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref), (b_max, int(np.sum(got != ref)))
