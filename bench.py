@@ -6,10 +6,12 @@ One step = the three 8B-shaped decode linears (4096->4096, 4096->14336,
 at about 3 effective bits, as three grinqh_gemv calls one after another (the
 order a decoder runs them in: each call is its own kernel launch doing bit
 assignment, prefix-plane streaming, midpoint dequant and the product).
-Inputs are resident in HBM before timing starts.  The steps rotate over
-enough packed weight copies (>= 512 MB) that the 256 MB Infinity Cache cannot
-hold them.  The timed region is one HIP graph holding exactly K steps,
-bracketed by device synchronisation and HIP events on the launch stream.
+Inputs are resident in HBM before timing starts.  Every timed launch
+rotates over enough packed weight copies that the plane bytes its linear
+reads over one rotation are at least twice the 256 MB Infinity Cache (sized
+at the fewest bits timed), so no launch finds its planes there.  The timed
+region is one HIP graph holding exactly K steps, bracketed by device
+synchronisation and HIP events on the launch stream.
 
 Reported value: required bytes per second, where required bytes = taken
 2-bit planes (sum_i b_i * d_out / 8) + fp16 s and z (4 * d_out), summed over
@@ -21,7 +23,7 @@ the step's GEMVs.  Also reported, each GEMV in its own launch unless stated:
  * b_max 4 (levels 0/2/4) at 1.5/2/3/4 effective bits, 4 being its dense mode;
  * b_max 6 (levels 0/2/4/6) at 2/3/4/6;
  * the 70B shapes (8192->8192, 8192->28672, 28672->8192) at 2 and 3 bits,
-   rotating over 8 weight copies (4.3 GB of planes);
+   rotating over weight copies sized the same way (about 7 GB of planes);
  * the whole 32-layer 8B decode step (128 launches in dependency order: per
    layer fused q|k|v, o, fused gate|up, down; 7.0 GB of planes at b_max 8) at
    2/3/4/6/8 bits, with its fit;
@@ -53,6 +55,7 @@ METRIC = "GEMV µs and required-bytes HBM GB/s (% of MI355X peak) at 2/3/4/8 eff
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
+MAX_COPIES = 256
 
 
 KERNEL_SOURCES = ("input_adaptive_bit_amd/csrc/gemv.hip", "input_adaptive_bit_amd/csrc/decode.hpp",
@@ -127,9 +130,14 @@ def fit_line(xs, ys):
 
 
 class Shape:
-    """One linear on the device: n_copies packed code copies (copy 0 from the
-    numpy generator, the rest drawn on the device), s, z, x, and a threshold
-    vector per effective-bits target (same codes, scales and x for all)."""
+    """One linear on the device: packed code copies (copy 0 from the numpy
+    generator, the rest drawn on the device), s, z, x, and a threshold vector
+    per effective-bits target (same codes, scales and x for all).
+
+    n_copies = 0 sizes the rotation by the bytes the launches actually read:
+    enough copies that one pass over them reads, at the fewest bits timed,
+    at least twice the 256 MB Infinity Cache (and at least 4 copies), so no
+    launch can find its planes there."""
 
     def __init__(self, spec, n_copies, dev, effs, host_codes=True):
         import torch
@@ -142,18 +150,7 @@ class Shape:
         self.s_np, self.z_np, self.x_f32 = lin.s, lin.z, lin.x
         self.L = G.grinqh_layout_init(spec.d_in, spec.d_out, spec.b_max)
         self.planes = []
-        for c in range(n_copies):
-            if c == 0 and host_codes:
-                qd = torch.from_numpy(lin.q).to(dev)
-            else:
-                g = torch.Generator(device=dev)
-                g.manual_seed(S.torch_seed(spec.key, 10 + c))
-                qd = torch.randint(0, 1 << spec.b_max, (spec.d_out, spec.d_in), generator=g, dtype=torch.uint8,
-                                   device=dev)
-            _, pl = G.pack(qd, spec.b_max)
-            self.planes.append(pl)
-            del qd
-        torch.cuda.synchronize()
+        self._add_copy(dev, lin.q if host_codes else None)
         self.s = torch.from_numpy(lin.s).to(dev)
         self.z = torch.from_numpy(lin.z).to(dev)
         self.x = torch.from_numpy(lin.x_bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
@@ -172,7 +169,28 @@ class Shape:
             b = bits.cpu().numpy()
             self.bits[eff] = b
             self.req[eff] = required_bytes(b, self.d_out)
+        if n_copies <= 0:
+            least = min(self.req[e] - 4.0 * self.d_out for e in effs)      # plane bytes read per launch
+            n_copies = min(MAX_COPIES, max(4, math.ceil(2 * MALL_BYTES / max(least, 1.0))))
+        while len(self.planes) < n_copies:
+            self._add_copy(dev, None)
+        torch.cuda.synchronize()
         self.n_copies = n_copies
+
+    def _add_copy(self, dev, q_host) -> None:
+        import torch
+        import input_adaptive_bit_amd as G
+        import synthetic as S
+        if q_host is not None:
+            qd = torch.from_numpy(q_host).to(dev)
+        else:
+            g = torch.Generator(device=dev)
+            g.manual_seed(S.torch_seed(self.spec.key, 10 + len(self.planes)))
+            qd = torch.randint(0, 1 << self.spec.b_max, (self.d_out, self.d_in), generator=g, dtype=torch.uint8,
+                               device=dev)
+        _, pl = G.pack(qd, self.spec.b_max)
+        self.planes.append(pl)
+        del qd
 
     def launch(self, copy: int, eff) -> None:
         import input_adaptive_bit_amd as G
@@ -290,7 +308,9 @@ def point(us: float, req: float, **extra) -> dict:
 
 def sweep_shapes(shapes, effs, reps, group=None, dense_key=None):
     """Per effective-bits target: each linear in its own launch, the linears
-    one after another (the step), and optionally one group launch."""
+    one after another (the step), and optionally one group launch.  A timed
+    graph holds at least one launch per weight copy, so it reads every copy."""
+    reps = max(reps, max(sh.n_copies for sh in shapes))
     out = {}
     for e in effs:
         row = {}
@@ -446,7 +466,8 @@ def main() -> int:
     ap.add_argument("--no-offline", action="store_true", help="skip calibration and RTN timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
-    ap.add_argument("--copies", type=int, default=0, help="weight copies (0: enough for 512 MB)")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="weight copies per linear (0: enough that one rotation reads twice the Infinity Cache)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run a plain elementwise fp32 kernel (torch.neg) that reads and "
                          "writes this many MiB, 4 times: the known-size reference for HBM byte counters")
@@ -470,11 +491,11 @@ def main() -> int:
     dev = torch.device("cuda:0")
     effs = (2, 3, 4, 8)
     per_eff_specs = {e: S.llama8b_linears(e) for e in effs}
-    set_bytes = sum(di * do for di, do in S.LLAMA8B_SHAPES)      # b_max 8: 1 byte per weight
-    n_copies = args.copies or max(1, math.ceil(2 * MALL_BYTES / set_bytes))
-    log(f"setup: {n_copies} weight copies of {set_bytes / 1e6:.1f} MB")
-    shapes = [Shape(per_eff_specs[args.eff][k], n_copies, dev, {e: per_eff_specs[e][k] for e in effs})
+    shapes = [Shape(per_eff_specs[args.eff][k], args.copies, dev, {e: per_eff_specs[e][k] for e in effs})
               for k in range(3)]
+    n_copies = {f"{sh.d_in}x{sh.d_out}": sh.n_copies for sh in shapes}
+    log(f"setup: weight copies {n_copies}, "
+        f"{sum(sh.n_copies * sh.d_in * sh.d_out for sh in shapes) / 1e9:.2f} GB of planes")
     eff = args.eff
 
     def steps_fn(n):
@@ -530,8 +551,7 @@ def main() -> int:
     if not args.no_sweep and not args.no_b4:
         effs4 = (1.5, 2, 3, 4)
         specs4 = {e: S.llama8b_linears_b4(e) for e in effs4}
-        n4 = max(1, math.ceil(2 * MALL_BYTES / (0.5 * set_bytes)))
-        shapes4 = [Shape(specs4[3][k], n4, dev, {e: specs4[e][k] for e in effs4}, host_codes=False)
+        shapes4 = [Shape(specs4[3][k], 0, dev, {e: specs4[e][k] for e in effs4}, host_codes=False)
                    for k in range(3)]
         log("sweep b_max 4:")
         sweep_b4 = sweep_shapes(shapes4, effs4, reps, dense_key=4)
@@ -547,8 +567,7 @@ def main() -> int:
     if not args.no_sweep and not args.no_b6:
         effs6 = (2, 3, 4, 6)
         specs6 = {e: S.llama8b_linears_b6(e) for e in effs6}
-        n6 = max(1, math.ceil(2 * MALL_BYTES / (0.75 * set_bytes)))
-        shapes6 = [Shape(specs6[3][k], n6, dev, {e: specs6[e][k] for e in effs6}, host_codes=False)
+        shapes6 = [Shape(specs6[3][k], 0, dev, {e: specs6[e][k] for e in effs6}, host_codes=False)
                    for k in range(3)]
         log("sweep b_max 6:")
         sweep_b6 = sweep_shapes(shapes6, effs6, reps, dense_key=6)
@@ -559,9 +578,10 @@ def main() -> int:
     if not args.no_sweep and not args.no_70b:
         effs70 = (2, 3)
         specs70 = {e: S.llama70b_linears(e) for e in effs70}
-        shapes70 = [Shape(specs70[3][k], 8, dev, {e: specs70[e][k] for e in effs70}, host_codes=False)
+        shapes70 = [Shape(specs70[3][k], 0, dev, {e: specs70[e][k] for e in effs70}, host_codes=False)
                     for k in range(3)]
-        log(f"70B shapes: 8 copies, {sum(sh.d_in * sh.d_out for sh in shapes70) * 8 / 1e9:.2f} GB of planes")
+        log(f"70B shapes: copies {[sh.n_copies for sh in shapes70]}, "
+            f"{sum(sh.n_copies * sh.d_in * sh.d_out for sh in shapes70) / 1e9:.2f} GB of planes")
         llama70b = sweep_shapes(shapes70, effs70, reps)
         del shapes70
         torch.cuda.empty_cache()
