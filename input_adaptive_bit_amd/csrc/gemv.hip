@@ -39,6 +39,8 @@
 // workgroup, which applies the epilogue y_j = s_j * acc_j + z_j * S (bf16
 // output rounded to nearest even) and clears its workspace row and counter
 // for the next call.
+#include <type_traits>
+
 #include "decode.hpp"
 #include "internal.h"
 
@@ -438,29 +440,46 @@ __device__ __forceinline__ void gemv_item(const GemvDesc& D, int item) {
         // a CU then keeps a part of its loads in the CU's queue instead of
         // all of them, so the resident workgroups are served side by side
         // rather than one after another.
-        // The four- and three-plane batches go out together and skip their
-        // empty slots (short buckets at the thresholds the method uses); the
-        // first decode then waits for both.  A launch of one workgroup per CU
-        // (G = 8) measured faster with the branch-free form.
-        constexpr bool kSkipEarly = G <= 4;
-        if constexpr (P >= 4) k4.template first<kSkipEarly>(L, start[3], start[4], wv, group, src);
-        if constexpr (P >= 3) k3.template first<kSkipEarly>(L, start[2], start[3], wv, group, src);
-        if constexpr (P <= 2) {
-            if constexpr (P >= 2) k2.first(L, start[1], start[2], wv, group, src);
-            // the last batch issued: when its bucket is empty (dense mode at
-            // b_max 4) it issues nothing, and the waits of the decode before
-            // it only gain loads that left at the same time
-            if (P == 1 || start[1] > start[0]) k1.first(L, start[0], start[1], wv, group, src);
+        auto general = [&](auto skip_early) {
+            constexpr bool kSkipEarly = decltype(skip_early)::value;
+            if constexpr (P >= 4) k4.template first<kSkipEarly>(L, start[3], start[4], wv, group, src);
+            if constexpr (P >= 3) k3.template first<kSkipEarly>(L, start[2], start[3], wv, group, src);
+            if constexpr (P <= 2) {
+                if constexpr (P >= 2) k2.first(L, start[1], start[2], wv, group, src);
+                // the last batch issued: when its bucket is empty (dense mode
+                // at b_max 4) it issues nothing, and the waits of the decode
+                // before it only gain loads that left at the same time
+                if (P == 1 || start[1] > start[0]) k1.first(L, start[0], start[1], wv, group, src);
+            }
+            slice_sums();
+            if constexpr (P >= 4) k4.finish(acc, L, group, src);
+            if constexpr (P >= 3) {
+                k2.first(L, start[1], start[2], wv, group, src);
+                k3.finish(acc, L, group, src);
+                k1.first(L, start[0], start[1], wv, group, src);
+            }
+            if constexpr (P >= 2) k2.finish(acc, L, group, src);
+            k1.finish(acc, L, group, src);
+        };
+        // When the four- and three-plane buckets each fit their first batch
+        // (short buckets, as at about 3 effective bits), those two batches,
+        // issued together, skip their empty slots and the first decode waits
+        // for both.  Fuller buckets have no empty slots to skip and keep the
+        // exact waits.  A launch of one workgroup per CU (G = 8) measured
+        // faster with the exact form.
+        bool skip_early = false;
+        constexpr int stride = kWaves * G;
+        if constexpr (P == 4 && G <= 4)
+            skip_early = start[4] - start[3] < BatchSize<P, 4>::U * stride &&
+                         start[3] - start[2] < BatchSize<P, 3>::U * stride;
+        else if constexpr (P == 3 && G <= 4)
+            skip_early = start[3] - start[2] < BatchSize<P, 3>::U * stride;
+        if constexpr (P >= 3 && G <= 4) {
+            if (skip_early) general(std::integral_constant<bool, true>{});
+            else general(std::integral_constant<bool, false>{});
+        } else {
+            general(std::integral_constant<bool, false>{});
         }
-        slice_sums();
-        if constexpr (P >= 4) k4.finish(acc, L, group, src);
-        if constexpr (P >= 3) {
-            k2.first(L, start[1], start[2], wv, group, src);
-            k3.finish(acc, L, group, src);
-            k1.first(L, start[0], start[1], wv, group, src);
-        }
-        if constexpr (P >= 2) k2.finish(acc, L, group, src);
-        k1.finish(acc, L, group, src);
     }
 
 
