@@ -265,6 +265,35 @@ struct Bucket {
         end = end_;
         load_batch<P, Pb, V, U, stride, kSkipEmpty>(B, &L.off[ew + group], group, end - ew, src);
     }
+    // The dense path's bucket (the only one loaded): the next batch is issued
+    // before the current one is decoded, so two batches are in flight.  The
+    // loop is unrolled by two so that each batch keeps its registers, and a
+    // batch is issued only when it has entries, so nothing is loaded past the
+    // bucket's end; each load sits in the block that decodes the batch before
+    // it, which keeps the waits exact.
+    __device__ __forceinline__ void finish_pipelined(float (&acc)[16 * V], const SliceLists& L, int group,
+                                                     const PlaneSrc& src) {
+        constexpr int S = stride * U;
+        Batch<Pb, V, U> B2;
+        int e = ew;
+        while (true) {
+            const int e2 = e + S;
+            if (e2 >= end) {
+                compute_batch<P, Pb, V, U, stride, true>(acc, B, &L.xv[e + group], group, end - e);
+                break;
+            }
+            load_batch<P, Pb, V, U, stride>(B2, &L.off[e2 + group], group, end - e2, src);
+            compute_batch<P, Pb, V, U, stride, false>(acc, B, &L.xv[e + group], group, end - e);
+            const int e3 = e2 + S;
+            if (e3 >= end) {
+                compute_batch<P, Pb, V, U, stride, true>(acc, B2, &L.xv[e2 + group], group, end - e2);
+                break;
+            }
+            load_batch<P, Pb, V, U, stride>(B, &L.off[e3 + group], group, end - e3, src);
+            compute_batch<P, Pb, V, U, stride, false>(acc, B2, &L.xv[e2 + group], group, end - e2);
+            e = e3;
+        }
+    }
     __device__ __forceinline__ void finish(float (&acc)[16 * V], const SliceLists& L, int group,
                                            const PlaneSrc& src) {
         compute_batch<P, Pb, V, U, stride, true>(acc, B, &L.xv[ew + group], group, end - ew);
@@ -428,11 +457,11 @@ __device__ __forceinline__ void gemv_item(const GemvDesc& D, int item) {
         if constexpr (P == 4) {
             k4.first(L, start[3], start[4], wv, group, src);
             slice_sums();
-            k4.finish(acc, L, group, src);
+            k4.finish_pipelined(acc, L, group, src);
         } else if constexpr (P == 3) {
             k3.first(L, start[2], start[3], wv, group, src);
             slice_sums();
-            k3.finish(acc, L, group, src);
+            k3.finish_pipelined(acc, L, group, src);
         }
     } else {
         // Two buckets in flight at a time: the next bucket's first batch is
