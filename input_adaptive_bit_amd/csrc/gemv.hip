@@ -23,7 +23,10 @@
 // untaken planes and skipped channels issue no memory request.  Every
 // channel in a bucket has the same plane count, so the lanes of a wave never
 // diverge.  Load batches are sized to hold a typical slice's share of a
-// bucket, and two buckets are in flight at a time.
+// bucket, and two buckets are in flight at a time.  A slice whose loaded
+// channels all take every plane (dense mode) streams only the top bucket,
+// two batches at a time; in other slices the first two batches skip their
+// empty slots when their buckets are short.
 //
 // Decode and accumulate (key design 3).  The Pi plane words of 16 outputs
 // become 16 exact floats (decode.hpp: packed FP4 / FP8 conversions for one and
