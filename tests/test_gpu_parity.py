@@ -684,3 +684,45 @@ def test_gemv_full_channel_slices_at_every_tile_width(dev, forced_shape, lane_gr
         torch.cuda.synchronize()
         got = y.cpu().numpy().astype(np.float64)
         assert np.array_equal(got, ref), (b_max, int(np.sum(got != ref)))
+
+
+def test_gemv_early_batch_forms_at_their_thresholds(dev, forced_shape):
+    """Slices whose four- and three-plane buckets sit just below and at the
+    sizes where the early batches switch from skipping empty slots to the
+    exact-wait form (32 and 48 entries at 4 lane groups, 256-channel slices):
+    exact integer sums against the oracle, with both forms in one launch."""
+    import torch
+    forced_shape(4, 256)
+    b_max, P = 8, 4
+    rng = np.random.default_rng(777)
+    # per 256-channel slice: (four-plane, three-plane) channel counts; the rest
+    # of the slice is split between one- and two-plane channels and skipped ones
+    plan = [(31, 47), (32, 47), (31, 48), (32, 48), (0, 0), (5, 60), (40, 10), (16, 24)]
+    theta = np.array([1.0, 2.0, 3.0, 4.0], np.float32)
+    mags = {4: [4.0, 5.0], 3: [3.0], 2: [2.0], 1: [1.0, 0.5 + 1.0], 0: [0.0, 0.5]}
+    x = []
+    for n4, n3 in plan:
+        rest = 256 - n4 - n3
+        lv = [4] * n4 + [3] * n3 + list(rng.choice([0, 1, 2], rest))
+        rng.shuffle(lv)
+        for l in lv:
+            m = rng.choice(mags[l])
+            x.append(m if rng.random() < 0.5 else -m)
+    x = np.array(x, np.float32)
+    d_in, d_out = x.size, 1536
+    q = rng.integers(0, 256, size=(d_out, d_in), dtype=np.uint8)
+    s = np.ones(d_out, np.float16)
+    z = np.ones(d_out, np.float16)
+    dl = DeviceLinear(q, s, z, b_max, dev)
+    say("early batch forms at their thresholds")
+    ref = C.gemv(x, theta, q, s, z, b_max)
+    assert np.max(np.abs(ref)) < 2 ** 23
+    bits = 2 * (theta[None, :] <= np.abs(x)[:, None]).sum(1)
+    for k, (n4, n3) in enumerate(plan):
+        seg = bits[k * 256:(k + 1) * 256]
+        assert (seg == 8).sum() == n4 and (seg == 6).sum() == n3
+    for rep in range(3):
+        y = dl.gemv(to_dev_x(x, "bf16", dev), _theta_dev(theta, dev), torch.float32)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref), (rep, int(np.sum(got != ref)))
